@@ -1,0 +1,107 @@
+/*
+ * sdattn.h -- C ABI of libsdattn: fused scaled dot-product attention for the
+ * transformer blocks of a diffusion UNet, on AMD MI355X (gfx950).
+ *
+ * Operation.  For every batch b < B, head h < H and query row i < Lq:
+ *
+ *     O[b,h,i,:] = sum_j softmax_j( scale * <Q[b,h,i,:], K[b,h,j,:]> ) V[b,h,j,:]
+ *
+ * This is the attention of the page "Diffusion inference engine from
+ * scratch: Rust + wgpu" (ybb.press), section 3.2: queries come from the
+ * latent feature map (HW tokens), keys and values either from the same map
+ * (self-attention) or from the 77-token CLIP text context (cross-attention),
+ * and the score matrix Q.K^T is never written to memory -- the softmax is
+ * evaluated block by block with a running maximum and running sum, which
+ * gives the plain softmax result up to rounding.  The scale is an explicit
+ * argument (1/sqrt(d) for the UNet; the pages do not print it).
+ *
+ * Layout.  q, k, v and out are contiguous row-major [B, H, L, d] device
+ * buffers: L = Lq for q and out, L = Lk (or Lctx) for k and v.  Keys and
+ * values carry their own batch index (classifier-free guidance concatenates
+ * the unconditional and conditional contexts along B; nothing is broadcast).
+ *
+ * Types (the dtype argument):
+ *   SDATTN_DTYPE_F32          fp32 q/k/v, fp32 out; fp32 arithmetic.
+ *   SDATTN_DTYPE_BF16         bf16 q/k/v, bf16 out (round to nearest even);
+ *                             bf16 matrix products with fp32 accumulation,
+ *                             the softmax weights are rounded to bf16 before
+ *                             the second product.
+ *   SDATTN_DTYPE_BF16_F32OUT  as SDATTN_DTYPE_BF16 but out is fp32.
+ *
+ * Ownership and synchronisation.  The caller owns every buffer and the
+ * stream.  The library allocates no device memory and needs no workspace.
+ * Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
+ * stream) and return without synchronising; buffers must stay alive until
+ * that work completes.  Inputs are read only; out must not overlap them.
+ * Calls are stateless and thread-safe.
+ *
+ * Errors.  Every function returns an sdattn_status; nothing is printed and
+ * no exception crosses the ABI.  Arguments are validated on the host before
+ * any HIP call.  A fault inside a kernel surfaces at the caller's next
+ * synchronisation of the stream, not as a return code.
+ */
+#ifndef SDATTN_H
+#define SDATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SDATTN_OK = 0,
+  SDATTN_ERR_INVALID_ARG = 1,  /* null pointer, B/H/Lq/Lk/d < 1, unknown dtype,
+                                  non-finite scale, out overlapping an input,
+                                  or a tensor larger than 2^31 - 1 elements */
+  SDATTN_ERR_UNSUPPORTED = 2,  /* d % 8 != 0, d > 256, or (cross entry) a
+                                  context longer than sdattn_cross_max_ctx */
+  SDATTN_ERR_MISALIGNED = 3,   /* a pointer not 16-byte aligned */
+  SDATTN_ERR_DEVICE = 4,       /* no HIP device, or the current device is
+                                  not gfx950 */
+  SDATTN_ERR_LAUNCH = 5        /* the kernel launch reported an error */
+} sdattn_status;
+
+typedef enum {
+  SDATTN_DTYPE_F32 = 0,
+  SDATTN_DTYPE_BF16 = 1,
+  SDATTN_DTYPE_BF16_F32OUT = 2
+} sdattn_dtype;
+
+/* Attention with any key length.  Internally dispatches to the short-key
+ * kernel (all keys resident in LDS, single-pass softmax) when
+ * Lk <= sdattn_cross_max_ctx(d, dtype), and to the streaming kernel
+ * (K/V tiles double-buffered through LDS, online softmax) otherwise.
+ * Used for UNet self-attention (Lk = Lq = HW). */
+int sdattn_fwd(const void *q, const void *k, const void *v, void *out, int B,
+               int H, int Lq, int Lk, int d, float scale, int dtype,
+               void *stream);
+
+/* Cross-attention to a short context (the text encoder's 77 tokens): always
+ * the short-key kernel; returns SDATTN_ERR_UNSUPPORTED when
+ * Lctx > sdattn_cross_max_ctx(d, dtype).  For Lctx within the cap the
+ * result is bit-identical to sdattn_fwd on the same arguments. */
+int sdattn_cross_fwd(const void *q, const void *ctx_k, const void *ctx_v,
+                     void *out, int B, int H, int Lq, int Lctx, int d,
+                     float scale, int dtype, void *stream);
+
+/* Attention that always takes the streaming (online-softmax) kernel, for
+ * any Lk >= 1.  For SDATTN_DTYPE_F32 this is the same kernel sdattn_fwd
+ * uses. */
+int sdattn_stream_fwd(const void *q, const void *k, const void *v, void *out,
+                      int B, int H, int Lq, int Lk, int d, float scale,
+                      int dtype, void *stream);
+
+/* Largest context length the short-key path accepts for this head dim and
+ * dtype; 0 if (d, dtype) is unsupported. */
+int sdattn_cross_max_ctx(int d, int dtype);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *sdattn_strerror(int status);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int sdattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDATTN_H */

@@ -1,0 +1,132 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+the header declares, and rejects bad arguments with the documented status
+before any HIP call."""
+import math
+import os
+import re
+
+import pytest
+
+import unet_attention_amd as sd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdattn.h")
+
+# Fake, 16-byte aligned addresses: validation fails before they are used.
+Q, K, V, O = 0x100000, 0x200000, 0x300000, 0x400000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdattn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sd.LIB_PATH):
+        pytest.skip("libsdattn.so not built")
+    return sd.load()
+
+
+def test_exports_every_header_symbol(lib):
+    names = header_functions()
+    assert "sdattn_fwd" in names and "sdattn_cross_fwd" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in sdattn.h but not exported"
+    assert set(names) == set(sd.EXPORTS), "binding and header disagree"
+
+
+def test_version_and_strerror(lib):
+    assert sd.sdattn_version() == 10000
+    seen = set()
+    for code in range(6):
+        msg = sd.sdattn_strerror(code)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert "unknown" in sd.sdattn_strerror(99)
+    assert "unknown" in sd.sdattn_strerror(-1)
+
+
+def test_cross_max_ctx(lib):
+    for dt in (sd.SDATTN_DTYPE_F32, sd.SDATTN_DTYPE_BF16, sd.SDATTN_DTYPE_BF16_F32OUT):
+        for d in (8, 40, 64, 80, 160, 256):
+            assert sd.sdattn_cross_max_ctx(d, dt) >= 77
+        for d in (0, 4, 41, 264, -8):
+            assert sd.sdattn_cross_max_ctx(d, dt) == 0
+    assert sd.sdattn_cross_max_ctx(40, 7) == 0
+
+
+def call(entry, **kw):
+    args = dict(q=Q, k=K, v=V, out=O, B=2, H=8, Lq=64, Lk=77, d=40,
+                scale=1 / math.sqrt(40), dtype=sd.SDATTN_DTYPE_BF16, stream=None)
+    args.update(kw)
+    fn = getattr(sd, entry)
+    return fn(args["q"], args["k"], args["v"], args["out"], args["B"], args["H"],
+              args["Lq"], args["Lk"], args["d"], args["scale"], args["dtype"],
+              args["stream"])
+
+
+ENTRIES = ["sdattn_fwd", "sdattn_cross_fwd", "sdattn_stream_fwd"]
+
+BAD = [
+    ("null_q", dict(q=None), sd.SDATTN_ERR_INVALID_ARG),
+    ("null_k", dict(k=None), sd.SDATTN_ERR_INVALID_ARG),
+    ("null_v", dict(v=None), sd.SDATTN_ERR_INVALID_ARG),
+    ("null_out", dict(out=None), sd.SDATTN_ERR_INVALID_ARG),
+    ("B0", dict(B=0), sd.SDATTN_ERR_INVALID_ARG),
+    ("H0", dict(H=0), sd.SDATTN_ERR_INVALID_ARG),
+    ("Lq0", dict(Lq=0), sd.SDATTN_ERR_INVALID_ARG),
+    ("Lk0", dict(Lk=0), sd.SDATTN_ERR_INVALID_ARG),
+    ("d0", dict(d=0), sd.SDATTN_ERR_INVALID_ARG),
+    ("negB", dict(B=-1), sd.SDATTN_ERR_INVALID_ARG),
+    ("dtype", dict(dtype=3), sd.SDATTN_ERR_INVALID_ARG),
+    ("dtype_neg", dict(dtype=-1), sd.SDATTN_ERR_INVALID_ARG),
+    ("nan_scale", dict(scale=float("nan")), sd.SDATTN_ERR_INVALID_ARG),
+    ("inf_scale", dict(scale=float("inf")), sd.SDATTN_ERR_INVALID_ARG),
+    ("too_big", dict(B=1 << 12, H=1 << 10, Lq=1 << 12), sd.SDATTN_ERR_INVALID_ARG),
+    ("d_odd", dict(d=41), sd.SDATTN_ERR_UNSUPPORTED),
+    ("d_12", dict(d=12), sd.SDATTN_ERR_UNSUPPORTED),
+    ("d_264", dict(d=264), sd.SDATTN_ERR_UNSUPPORTED),
+    ("misaligned_q", dict(q=Q + 2), sd.SDATTN_ERR_MISALIGNED),
+    ("misaligned_k", dict(k=K + 8), sd.SDATTN_ERR_MISALIGNED),
+    ("misaligned_v", dict(v=V + 4), sd.SDATTN_ERR_MISALIGNED),
+    ("misaligned_out", dict(out=O + 2), sd.SDATTN_ERR_MISALIGNED),
+    ("out_is_q", dict(out=Q), sd.SDATTN_ERR_INVALID_ARG),
+    ("out_overlaps_k_tail", dict(out=K - 16), sd.SDATTN_ERR_INVALID_ARG),
+    ("out_overlaps_v", dict(out=V + 64), sd.SDATTN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("case", BAD, ids=[b[0] for b in BAD])
+def test_invalid_arguments(lib, entry, case):
+    _, kw, want = case
+    assert call(entry, **kw) == want
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+def test_cross_rejects_long_context(lib, dtype):
+    cap = sd.sdattn_cross_max_ctx(40, dtype)
+    assert call("sdattn_cross_fwd", Lk=cap + 1, dtype=dtype) == sd.SDATTN_ERR_UNSUPPORTED
+
+
+def _gpu_present():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_valid_call_without_gpu_reports_device(lib, entry):
+    if _gpu_present():
+        pytest.skip("a GPU is present; fake pointers must not reach a launch")
+    assert call(entry) == sd.SDATTN_ERR_DEVICE
+
+
+def test_torch_wrapper_checks_shapes(lib):
+    import torch
+    q = torch.zeros(1, 1, 4, 8)
+    with pytest.raises(ValueError):
+        sd.fwd(q, q, q)  # CPU tensors are refused before any call
+    with pytest.raises(ValueError):
+        sd.fwd(q.to(torch.float16), q, q)

@@ -1,0 +1,162 @@
+"""Python binding of libsdattn (fused UNet attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libsdattn.so``.  The raw functions keep the C names and take
+integer device pointers and a ``hipStream_t`` (as an int, 0 = default
+stream); ``fwd`` / ``cross_fwd`` / ``stream_fwd`` accept torch tensors on
+the ROCm device and use torch only for buffers and the current stream.
+
+The library must have been built (``__graft_entry__.build()`` or
+``python unet_attention_amd/build.py``); loading fails loudly otherwise --
+there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsdattn.so")
+
+SDATTN_OK = 0
+SDATTN_ERR_INVALID_ARG = 1
+SDATTN_ERR_UNSUPPORTED = 2
+SDATTN_ERR_MISALIGNED = 3
+SDATTN_ERR_DEVICE = 4
+SDATTN_ERR_LAUNCH = 5
+
+SDATTN_DTYPE_F32 = 0
+SDATTN_DTYPE_BF16 = 1
+SDATTN_DTYPE_BF16_F32OUT = 2
+
+# Every function the C header declares, with its ctypes signature.
+_VP = ctypes.c_void_p
+_I = ctypes.c_int
+_ATTN_ARGS = [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_float, _I, _VP]
+EXPORTS = {
+    "sdattn_fwd": (_I, _ATTN_ARGS),
+    "sdattn_cross_fwd": (_I, _ATTN_ARGS),
+    "sdattn_stream_fwd": (_I, _ATTN_ARGS),
+    "sdattn_cross_max_ctx": (_I, [_I, _I]),
+    "sdattn_strerror": (ctypes.c_char_p, [_I]),
+    "sdattn_version": (_I, []),
+}
+
+
+class SdattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sdattn_strerror(status)} (status {status})")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsdattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(
+                f"{path} is missing: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# raw C ABI (same names and argument order as include/sdattn.h)
+
+def sdattn_fwd(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, stream):
+    return load().sdattn_fwd(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, stream)
+
+
+def sdattn_cross_fwd(q, ctx_k, ctx_v, out, B, H, Lq, Lctx, d, scale, dtype, stream):
+    return load().sdattn_cross_fwd(q, ctx_k, ctx_v, out, B, H, Lq, Lctx, d,
+                                   scale, dtype, stream)
+
+
+def sdattn_stream_fwd(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, stream):
+    return load().sdattn_stream_fwd(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, stream)
+
+
+def sdattn_cross_max_ctx(d, dtype):
+    return load().sdattn_cross_max_ctx(d, dtype)
+
+
+def sdattn_strerror(status):
+    return load().sdattn_strerror(status).decode()
+
+
+def sdattn_version():
+    return load().sdattn_version()
+
+
+# ---------------------------------------------------------------------------
+# torch tensors in, torch tensors out
+
+_ENTRIES = {"auto": "sdattn_fwd", "cross": "sdattn_cross_fwd",
+            "stream": "sdattn_stream_fwd"}
+
+
+def _call(entry, q, k, v, out=None, scale=None, out_dtype=None, stream=None):
+    import torch
+    if q.dtype == torch.float32:
+        dtype_code = SDATTN_DTYPE_F32
+        odt = torch.float32
+        if out_dtype not in (None, torch.float32):
+            raise ValueError("fp32 inputs produce fp32 output")
+    elif q.dtype == torch.bfloat16:
+        odt = out_dtype or torch.bfloat16
+        if odt == torch.bfloat16:
+            dtype_code = SDATTN_DTYPE_BF16
+        elif odt == torch.float32:
+            dtype_code = SDATTN_DTYPE_BF16_F32OUT
+        else:
+            raise ValueError(f"unsupported output dtype {odt}")
+    else:
+        raise ValueError(f"unsupported input dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d device tensor [B,H,L,d]")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if tuple(k.shape) != (B, H, Lk, d) or tuple(v.shape) != (B, H, Lk, d):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out is None:
+        out = torch.empty((B, H, Lq, d), dtype=odt, device=q.device)
+    elif out.dtype != odt or tuple(out.shape) != (B, H, Lq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,H,Lq,d] tensor of the output dtype")
+    if scale is None:
+        scale = float(1.0 / math.sqrt(d))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    fn = getattr(load(), _ENTRIES[entry])
+    rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            B, H, Lq, Lk, d, scale, dtype_code, stream)
+    if rc != SDATTN_OK:
+        raise SdattnError(rc, _ENTRIES[entry])
+    return out
+
+
+def fwd(q, k, v, out=None, scale=None, out_dtype=None, stream=None):
+    """softmax(scale * Q K^T) V via sdattn_fwd (short-key or streaming kernel)."""
+    return _call("auto", q, k, v, out, scale, out_dtype, stream)
+
+
+def cross_fwd(q, ctx_k, ctx_v, out=None, scale=None, out_dtype=None, stream=None):
+    """Cross-attention to a short context via sdattn_cross_fwd."""
+    return _call("cross", q, ctx_k, ctx_v, out, scale, out_dtype, stream)
+
+
+def stream_fwd(q, k, v, out=None, scale=None, out_dtype=None, stream=None):
+    """Always the streaming (online-softmax) kernel, via sdattn_stream_fwd."""
+    return _call("stream", q, k, v, out, scale, out_dtype, stream)

@@ -1,0 +1,95 @@
+// attn_common.hpp -- device-side types and helpers shared by the bf16 and
+// fp32 attention kernels of libsdattn (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;           // CDNA wavefront width
+constexpr int kQW = 32;             // query rows owned by one wave (bf16 kernels)
+constexpr float kLog2e = 1.4426950408889634f;
+// Lazy rescaling: the running maximum m (log2 domain) is only raised when a
+// tile's maximum exceeds it by more than this many binary orders, so the
+// unnormalised weights stay <= 2^kRescaleSlack.  The result is unchanged in
+// exact arithmetic because l and O always share the same stale m.
+constexpr float kRescaleSlack = 8.0f;
+
+// Arguments common to the bf16 kernels.  Pointers are [B, H, L, d]
+// contiguous; q/k/v hold bf16 bit patterns.
+struct Bf16Args {
+  const uint16_t *q;
+  const uint16_t *k;
+  const uint16_t *v;
+  void *out;
+  int Lq, Lk, d;
+  int qblocks;     // workgroups per (b, h)
+  int nwg;         // total workgroups
+  float c;         // |scale| * log2(e): scores enter exp2 as s * c
+  uint32_t qsign;  // 0x80008000 flips Q's sign bits when scale < 0
+};
+
+struct F32Args {
+  const float *q;
+  const float *k;
+  const float *v;
+  float *out;
+  int Lq, Lk, d;
+  int qblocks;
+  float scale;
+};
+
+// The dispatcher hands workgroup i to XCD (i mod 8).  Renumber so that the
+// workgroups resident on one XCD get consecutive logical ids, i.e. the
+// query blocks of one (b, h) share that XCD's L2 copy of its K and V.
+// A bijection on [0, n) for every n.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int per = n >> 3, rem = n & 7;
+  const int x = i & 7, k = i >> 3;
+  return (x < rem) ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
+}
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).
+// Lane l supplies row (l % 32) of A / column (l % 32) of B with eight
+// consecutive k values; the accumulator gives lane l column (l % 32) and
+// rows 8*(i/4) + 4*(l/32) + (i%4) for register i.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) {
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ void st16(void *p, u32x4 x) {
+  *reinterpret_cast<u32x4 *>(p) = x;
+}
+
+// Exchange a value with the lane 32 positions away (the other half-wave).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+// bf16 bits of two floats packed low/high, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+}  // namespace sdattn

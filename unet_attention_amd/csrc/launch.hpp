@@ -1,0 +1,21 @@
+// launch.hpp -- internal launchers between the C ABI (sdattn_api.hip) and
+// the kernels.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "attn_common.hpp"
+
+namespace sdattn {
+
+// Largest key count the short-key (all keys in LDS) bf16 kernel takes.
+int short_path_max_keys();
+
+// bf16 kernels.  a.qblocks and a.nwg are filled in by the launcher.
+hipError_t launch_bf16(const Bf16Args &a, int BH, bool short_path, bool out_f32,
+                       hipStream_t stream);
+
+// fp32 kernel (any Lk).
+hipError_t launch_f32(const F32Args &a, int BH, hipStream_t stream);
+
+}  // namespace sdattn
