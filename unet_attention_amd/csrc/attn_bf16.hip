@@ -7,7 +7,8 @@
 // memory) target Vulkan/Metal-class GPUs; the design here is CDNA4's own:
 //
 // * one wave owns 32 query rows; both products run on the 32x32x16 bf16
-//   matrix cores with fp32 accumulation;
+//   matrix cores with fp32 accumulation, in VGPR form (two waves per SIMD,
+//   so no accumulator shuffling through AGPRs);
 // * scores are produced transposed, S^T = K Q^T, so lane l holds the scores
 //   of query (l % 32) against 16 keys of each 32-key sub-tile: the row
 //   maximum and row sum are in-lane plus one exchange between half-waves;
@@ -15,15 +16,21 @@
 //   operand of O^T += V^T P^T, so the weights never leave registers; V is
 //   stored transposed in LDS with its keys in the matching order;
 // * the running maximum lives in the log2 domain (exp2 with scale*log2(e)
-//   folded into one FMA) and is raised lazily, only when a tile's maximum
+//   folded into one FMA) and is raised lazily, only when a sub-tile's maximum
 //   exceeds it by kRescaleSlack binary orders;
-// * when the head dim is padded (d = 40 -> 64, 80 -> 96 columns of V^T), a
-//   row of ones in the padding makes the matrix core produce the row sum l
-//   for free;
+// * when the head dim is padded (d = 40 -> 64, 80 -> 96 rows of V^T), a row
+//   of ones in the padding makes the matrix core produce the row sum l;
+// * K, V and Q are read with range-checked buffer loads: rows past the end
+//   read as zero, and every address is a loop-invariant register plus an
+//   immediate;
 // * streaming kernel: K and V^T tiles of 64 keys double-buffered in LDS,
-//   prefetched into registers one tile ahead, one barrier per tile;
+//   prefetched into registers one tile ahead, one barrier per tile, the loop
+//   unrolled by two so both LDS buffers have fixed addresses, and the ragged
+//   last tile handled by a separately compiled masked step;
 //   short-key kernel (text contexts, Lk <= 128): all keys loaded to LDS
 //   once, single-pass softmax with no rescaling.
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -31,9 +38,21 @@ namespace sdattn {
 
 namespace {
 
-constexpr int kBN = 64;        // keys per streamed tile
 constexpr int kShortMax = 128;  // keys held by the short-key kernel
 constexpr uint16_t kBf16One = 0x3F80;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer, range checked
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                           (int)bytes, kRsrcWord3);
+}
+
+// 16-byte load; a chunk at or past the buffer's size reads as zero.
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
 template <int DK>
 struct Shape {
@@ -41,21 +60,32 @@ struct Shape {
   static constexpr bool kOnes = (DV > DK);         // padding holds a ones row
   static constexpr int DK8 = DK / 8;               // 16-byte chunks per row
   static constexpr int KST = DK + 8;               // K row stride in LDS
+  static constexpr int MT = DV / 32;               // O^T accumulator tiles
 };
+
+// Two waves per SIMD keep the whole working set in <= 256 VGPRs (VGPR-form
+// MFMA); the widest head dims need more registers and run one wave per SIMD.
+template <int DK>
+constexpr int waves_per_simd() { return DK <= 112 ? 2 : 1; }
+
+// Minimum resident workgroups per CU that gives waves_per_simd() (4 SIMDs).
+template <int DK, int NW>
+constexpr int min_blocks() {
+  return (4 * waves_per_simd<DK>() / NW) > 0 ? 4 * waves_per_simd<DK>() / NW : 1;
+}
 
 // Q fragments: B operand of S^T = K Q^T.  Lane l holds query q0 + l%32 and
 // columns dk*16 + 8*(l/32) .. +7; rows past Lq and columns past d are zero.
 template <int DK>
-__device__ __forceinline__ void load_q(bf16x8 (&qf)[DK / 16],
-                                       const uint16_t *qg, int q0, int Lq,
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[DK / 16], rsrc_t qr, int q0,
                                        int d, uint32_t qsign, int lane) {
   const int qi = q0 + (lane & 31);
   const int cb = 8 * (lane >> 5);
 #pragma unroll
   for (int dk = 0; dk < DK / 16; ++dk) {
     const int c0 = dk * 16 + cb;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < Lq && c0 < d) x = ld16(qg + (size_t)qi * d + c0);
+    u32x4 x = bload16(qr, (uint32_t)(qi * d + c0) * 2u);
+    if (c0 >= d) x = u32x4{0u, 0u, 0u, 0u};
     x ^= qsign;
     qf[dk] = as_bf16x8(x);
   }
@@ -71,72 +101,57 @@ __device__ __forceinline__ void store_vt_unit(uint16_t *vt, int vst, int row0,
   const int slot = kc * 16 + 8 * (gg & 1) + 4 * (gg >> 1);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    // v_perm_b32 byte selectors: {low halves of a, b} or {high halves}.
     const int w = i >> 1;
-    uint32_t lo, hi;
-    if (i & 1) {
-      lo = (rows[0][w] >> 16) | (rows[1][w] & 0xFFFF0000u);
-      hi = (rows[2][w] >> 16) | (rows[3][w] & 0xFFFF0000u);
-    } else {
-      lo = (rows[0][w] & 0xFFFFu) | (rows[1][w] << 16);
-      hi = (rows[2][w] & 0xFFFFu) | (rows[3][w] << 16);
-    }
-    u32x2 pr = {lo, hi};
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+    u32x2 pr = {__builtin_amdgcn_perm(rows[1][w], rows[0][w], sel),
+                __builtin_amdgcn_perm(rows[3][w], rows[2][w], sel)};
     *reinterpret_cast<u32x2 *>(vt + (row0 + i) * vst + slot) = pr;
   }
 }
 
 // Rows [d, DV) of V^T never change: zeros, plus a row of ones at d when the
-// row sum is taken from the matrix core.
-template <int DK>
-__device__ __forceinline__ void init_vt_const(uint16_t *vt, int vst, int keys,
-                                              int d, int tid, int nthreads) {
+// row sum is taken from the matrix core.  KEYS slots per row are written.
+template <int DK, int KEYS>
+__device__ __forceinline__ void init_vt_const(uint16_t *vt, int vst, int d, int tid,
+                                              int nthreads) {
   using S = Shape<DK>;
-  const int per_row = keys / 8;
+  constexpr int per_row = KEYS / 8;
   const int n = (S::DV - d) * per_row;
   for (int idx = tid; idx < n; idx += nthreads) {
     const int r = d + idx / per_row, c8 = idx % per_row;
     const uint32_t w = (S::kOnes && r == d) ? (uint32_t(kBf16One) * 0x10001u) : 0u;
-    u32x4 x = {w, w, w, w};
-    st16(vt + r * vst + c8 * 8, x);
+    st16(vt + r * vst + c8 * 8, u32x4{w, w, w, w});
   }
 }
 
-// K pad columns [d, DK) are zero in every row.
-template <int DK>
-__device__ __forceinline__ void init_k_pad(uint16_t *ks, int rows, int d,
-                                           int tid, int nthreads) {
+// K pad columns [d, DK) are zero in every row.  d is a multiple of 8 and DK
+// the next multiple of 16, so there is at most one 16-byte pad chunk.
+template <int DK, int ROWS>
+__device__ __forceinline__ void init_k_pad(uint16_t *ks, int d, int tid, int nthreads) {
   using S = Shape<DK>;
-  const int d8 = d >> 3, padc = S::DK8 - d8;
-  const int n = rows * padc;
-  for (int idx = tid; idx < n; idx += nthreads) {
-    const int r = idx / padc, c = d8 + idx % padc;
-    st16(ks + r * S::KST + c * 8, u32x4{0u, 0u, 0u, 0u});
-  }
+  if ((d >> 3) == S::DK8) return;
+  for (int r = tid; r < ROWS; r += nthreads)
+    st16(ks + r * S::KST + (S::DK8 - 1) * 8, u32x4{0u, 0u, 0u, 0u});
 }
 
 // One 32-key sub-tile of S^T for this wave: sum over head-dim chunks.
 template <int DK>
-__device__ __forceinline__ f32x16 scores_subtile(const uint16_t *ks, int row0,
-                                                 const bf16x8 (&qf)[DK / 16],
-                                                 int lane) {
-  using S = Shape<DK>;
+__device__ __forceinline__ f32x16 scores_subtile(const uint16_t *kp,
+                                                 const bf16x8 (&qf)[DK / 16]) {
   f32x16 acc = {};
-  const uint16_t *kp = ks + (row0 + (lane & 31)) * S::KST + 8 * (lane >> 5);
 #pragma unroll
   for (int dk = 0; dk < DK / 16; ++dk)
     acc = mfma32x32x16(as_bf16x8(ld16(kp + dk * 16)), qf[dk], acc);
   return acc;
 }
 
-// O^T += V^T P^T over one 16-key chunk (keys kc*16 .. +15 of the LDS tile).
+// O^T += V^T P^T over one 16-key chunk; vp points at this lane's row/slot.
 template <int DK>
-__device__ __forceinline__ void pv_chunk(f32x16 (&o)[Shape<DK>::DV / 32],
-                                         const uint16_t *vt, int vst, int kc,
-                                         bf16x8 p, int lane) {
-  using S = Shape<DK>;
-  const uint16_t *vp = vt + (lane & 31) * vst + kc * 16 + 8 * (lane >> 5);
+__device__ __forceinline__ void pv_chunk(f32x16 (&o)[Shape<DK>::MT],
+                                         const uint16_t *vp, int vst, bf16x8 p) {
 #pragma unroll
-  for (int mt = 0; mt < S::DV / 32; ++mt)
+  for (int mt = 0; mt < Shape<DK>::MT; ++mt)
     o[mt] = mfma32x32x16(as_bf16x8(ld16(vp + mt * 32 * vst)), p, o[mt]);
 }
 
@@ -145,9 +160,61 @@ __device__ __forceinline__ int acc_key(int i, int lane) {
   return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
+// Sequential chain: compiles to v_max3_f32, two new values per instruction.
+__device__ __forceinline__ float max16(const f32x16 &s, float m) {
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) m = fmaxf(fmaxf(m, s[i]), s[i + 1]);
+  return m;
+}
+
+// Online-softmax update for one 32-key sub-tile followed by its two P.V
+// chunks.  key0 is the sub-tile's first key; vp points at the sub-tile's
+// first 16-key chunk of V^T for this lane.
+template <int DK, bool MASK>
+__device__ __forceinline__ void softmax_pv(f32x16 &s, int key0, int Lk, float c,
+                                           float &m_run, float &lsum,
+                                           f32x16 (&o)[Shape<DK>::MT],
+                                           const uint16_t *vp, int vst, int lane) {
+  using S = Shape<DK>;
+  if constexpr (MASK) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (key0 + acc_key(i, lane) >= Lk) s[i] = -__builtin_inff();
+  }
+  float mx = max16(s, -__builtin_inff());
+  mx = max_halves(mx);
+  const float mt_new = mx * c;
+  if (__any(mt_new > m_run + kRescaleSlack)) {
+    const float mn = fmaxf(m_run, mt_new);
+    const float alpha = fast_exp2(m_run - mn);
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt) o[mt] *= alpha;
+    lsum *= alpha;
+    m_run = mn;
+  }
+  const float nm = -m_run;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = 8 * kk + j;
+      float x = fast_exp2(__builtin_fmaf(s[i], c, nm));
+      if constexpr (MASK) {
+        if (key0 + acc_key(i, lane) >= Lk) x = 0.f;
+      }
+      p[j] = x;
+      if constexpr (!S::kOnes) lsum += x;
+    }
+    const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    pv_chunk<DK>(o, vp + kk * 16, vst, as_bf16x8(pk));
+  }
+}
+
 // Epilogue: divide by the row sum and store this wave's 32 rows.
 template <int DK, bool OUT_F32>
-__device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::DV / 32],
+__device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::MT],
                                           float lsum, void *outp, size_t obase,
                                           int q0, int Lq, int d, int lane) {
   using S = Shape<DK>;
@@ -156,20 +223,20 @@ __device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::DV / 32],
     // Row d of O^T holds sum_j p_j; it sits in the first half-wave.
     float lv = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < S::DV / 32; ++mt)
+    for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
         if (mt * 32 + 8 * g4 == d) lv = o[mt][4 * g4];
-    l = __shfl(lv, lane & 31);
+    l = from_low_half(lv);
   } else {
-    l = lsum + swap_halves(lsum);
+    l = sum_halves(lsum);
   }
   const float inv = 1.0f / l;
   const int qi = q0 + (lane & 31);
   if (qi >= Lq) return;
   const int hb = 4 * (lane >> 5);
 #pragma unroll
-  for (int mt = 0; mt < S::DV / 32; ++mt)
+  for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int c0 = mt * 32 + 8 * g4 + hb;
@@ -191,135 +258,243 @@ __device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::DV / 32],
 // ---------------------------------------------------------------------------
 // Streaming kernel: any Lk >= 1.
 
-template <int DK, int NW, bool OUT_F32>
-__global__ __launch_bounds__(NW * kWave) void attn_stream_bf16(Bf16Args a) {
+// Streaming schedule: software-pipelined (scores of tile t+1 issued before
+// the softmax of tile t, three K buffers) or plain double buffering.
+#ifndef SDATTN_STREAM_PIPELINED
+#define SDATTN_STREAM_PIPELINED 0
+#endif
+constexpr bool kPipelined = SDATTN_STREAM_PIPELINED != 0;
+
+// Keys per streamed tile: 64, or 32 for the widest head dims so that three
+// K buffers and two V^T buffers stay within the 160 KB of LDS.
+template <int DK>
+constexpr int stream_bn() { return DK <= 224 ? 64 : 32; }
+
+template <int DK, int NW>
+struct StreamPlan {
   using S = Shape<DK>;
-  constexpr int NT = NW * kWave;
-  constexpr int VST = kBN + 8;
-  constexpr int KCH = (kBN * S::DK8 + NT - 1) / NT;
-  constexpr int VU = (kBN / 4) * S::DK8;
-  constexpr int VCH = (VU + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * S::KST];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][S::DV * VST];
+  static constexpr int BN = stream_bn<DK>();
+  static constexpr int NSUB = BN / 32;                       // 32-key sub-tiles
+  static constexpr int NT = NW * kWave;
+  static constexpr int VST = BN + 8;                         // V^T row stride
+  static constexpr int KCH = (BN * S::DK8 + NT - 1) / NT;    // K chunks / thread
+  static constexpr int VG = BN / 4;                          // 4-key groups
+  static constexpr int VCH = (VG * S::DK8 + NT - 1) / NT;    // V units / thread
+  static constexpr int KBUF = BN * S::KST;                   // elements per K buffer
+  static constexpr int VBUF = S::DV * VST;                   // elements per V^T buffer
+};
+
+// Per-thread staging state: which K chunks and V units this thread moves
+// from HBM/L2 into LDS.  K chunks are handed out from the first wave, V
+// units from the last, so the two jobs land on different waves.
+template <int DK, int NW>
+struct Stager {
+  using P = StreamPlan<DK, NW>;
+  uint32_t k_goff[P::KCH];   // byte offset within a tile (global)
+  int k_loff[P::KCH];        // element offset in an LDS K buffer, -1 = idle
+  uint32_t v_goff[P::VCH];   // byte offset of the unit's first row within a tile
+  int v_row0[P::VCH];        // first V^T row (column of V), -1 = idle
+  int v_g[P::VCH];           // 4-key group
+  u32x4 kreg[P::KCH];
+  u32x4 vreg[P::VCH][4];
+
+  __device__ __forceinline__ void init(int tid, int d) {
+    const int d8 = d >> 3;
+#pragma unroll
+    for (int t = 0; t < P::KCH; ++t) {
+      const int idx = tid + t * P::NT;
+      const int row = idx / d8, ch = idx - row * d8;
+      const bool ok = idx < P::BN * d8;
+      k_goff[t] = (uint32_t)idx * 16u;
+      k_loff[t] = ok ? row * Shape<DK>::KST + ch * 8 : -1;
+    }
+#pragma unroll
+    for (int t = 0; t < P::VCH; ++t) {
+      const int u = (P::NT - 1 - tid) + t * P::NT;
+      const int g = u % P::VG, ch = u / P::VG;
+      const bool ok = u < P::VG * d8;
+      v_goff[t] = (uint32_t)(4 * g * d + ch * 8) * 2u;
+      v_row0[t] = ok ? ch * 8 : -1;
+      v_g[t] = g;
+    }
+  }
+
+  // Issue the loads of the K / V tile starting at key j0 (rows >= Lk read
+  // zero through the buffer range check).
+  __device__ __forceinline__ void load_k(rsrc_t kr, int j0, int d) {
+    const uint32_t base = (uint32_t)(j0 * d) * 2u;
+#pragma unroll
+    for (int t = 0; t < P::KCH; ++t)
+      if (k_loff[t] >= 0) kreg[t] = bload16(kr, base + k_goff[t]);
+  }
+  __device__ __forceinline__ void load_v(rsrc_t vr, int j0, int d) {
+    const uint32_t base = (uint32_t)(j0 * d) * 2u, row = (uint32_t)d * 2u;
+#pragma unroll
+    for (int t = 0; t < P::VCH; ++t)
+      if (v_row0[t] >= 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vreg[t][r] = bload16(vr, base + v_goff[t] + r * row);
+      }
+  }
+  __device__ __forceinline__ void store_k(uint16_t *ks) {
+#pragma unroll
+    for (int t = 0; t < P::KCH; ++t)
+      if (k_loff[t] >= 0) st16(ks + k_loff[t], kreg[t]);
+  }
+  __device__ __forceinline__ void store_v(uint16_t *vt) {
+#pragma unroll
+    for (int t = 0; t < P::VCH; ++t)
+      if (v_row0[t] >= 0) store_vt_unit(vt, P::VST, v_row0[t], v_g[t], vreg[t]);
+  }
+};
+
+// Software pipeline, per iteration t (one tile of BN keys):
+//   issue the HBM/L2 loads of K[t+2] and V[t+1] into registers;
+//   S[t+1] = K[t+1] Q^T on the matrix cores (asynchronous) while the vector
+//   ALUs run the softmax of S[t] (computed in the previous iteration);
+//   O^T += V[t]^T P[t]^T;
+//   write K[t+2], V[t+1] to LDS; one barrier.
+// K cycles through three LDS buffers (t+1 is read while t+2 is written and
+// t's buffer may still be read by a slower wave), V^T through two.
+template <int DK, int NW, bool OUT_F32>
+__global__ __launch_bounds__(NW * kWave, (min_blocks<DK, NW>()))
+void attn_stream_bf16(Bf16Args a) {
+  using S = Shape<DK>;
+  using P = StreamPlan<DK, NW>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[(kPipelined ? 3 : 2) * P::KBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * P::VBUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = xcd_remap(blockIdx.x, a.nwg);
   const int bh = wg / a.qblocks;
   const int q0 = (wg - bh * a.qblocks) * (NW * kQW) + wave * kQW;
-  const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
-  const uint16_t *kg = a.k + (size_t)bh * Lk * d;
-  const uint16_t *vg = a.v + (size_t)bh * Lk * d;
+  const int d = a.d, Lk = a.Lk, Lq = a.Lq;
   const float c = a.c;
+  const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
+  const rsrc_t kr = make_rsrc(a.k + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  const rsrc_t vr = make_rsrc(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  constexpr int BN = P::BN, NSUB = P::NSUB;
+  const int ntiles = (Lk + BN - 1) / BN;
+  const bool ragged = (Lk % BN) != 0;
+
+  Stager<DK, NW> st;
+  st.init(tid, d);
+  st.load_k(kr, 0, d);
+  st.load_v(vr, 0, d);
 
   bf16x8 qf[DK / 16];
-  load_q<DK>(qf, a.q + (size_t)bh * Lq * d, q0, Lq, d, a.qsign, lane);
+  load_q<DK>(qf, qr, q0, d, a.qsign, lane);
 
-  init_k_pad<DK>(&Ks[0][0], 2 * kBN, d, tid, NT);
-  init_vt_const<DK>(&Vt[0][0], VST, kBN, d, tid, NT);
-  init_vt_const<DK>(&Vt[1][0], VST, kBN, d, tid, NT);
+  init_k_pad<DK, (kPipelined ? 3 : 2) * BN>(Ks, d, tid, P::NT);
+  init_vt_const<DK, BN>(Vt, P::VST, d, tid, P::NT);
+  init_vt_const<DK, BN>(Vt + P::VBUF, P::VST, d, tid, P::NT);
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[VCH][4];
-  auto load_tile = [&](int j0) {
-#pragma unroll
-    for (int t = 0; t < KCH; ++t) {
-      const int idx = tid + t * NT;
-      const int row = idx / S::DK8, ch = idx % S::DK8, j = j0 + row;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (idx < kBN * S::DK8 && ch < d8 && j < Lk) x = ld16(kg + (size_t)j * d + ch * 8);
-      kreg[t] = x;
-    }
-#pragma unroll
-    for (int t = 0; t < VCH; ++t) {
-      const int u = tid + t * NT;
-      const int g = u % (kBN / 4), ch = u / (kBN / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 4 * g + r;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (u < VU && ch < d8 && j < Lk) x = ld16(vg + (size_t)j * d + ch * 8);
-        vreg[t][r] = x;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int t = 0; t < KCH; ++t) {
-      const int idx = tid + t * NT;
-      const int row = idx / S::DK8, ch = idx % S::DK8;
-      if (idx < kBN * S::DK8 && ch < d8) st16(&Ks[buf][row * S::KST + ch * 8], kreg[t]);
-    }
-#pragma unroll
-    for (int t = 0; t < VCH; ++t) {
-      const int u = tid + t * NT;
-      const int g = u % (kBN / 4), ch = u / (kBN / 4);
-      if (u < VU && ch < d8) store_vt_unit(&Vt[buf][0], VST, ch * 8, g, vreg[t]);
-    }
-  };
+  st.store_k(Ks);
+  st.store_v(Vt);
+  if (kPipelined && ntiles > 1) {
+    st.load_k(kr, BN, d);
+    st.store_k(Ks + P::KBUF);
+  }
+  __syncthreads();
 
-  f32x16 o[S::DV / 32];
+  // Per-lane LDS read bases: K rows (l % 32), V^T rows (l % 32).
+  const int koff = (lane & 31) * S::KST + 8 * (lane >> 5);
+  const int voff = (lane & 31) * P::VST + 8 * (lane >> 5);
+
+  f32x16 o[S::MT];
 #pragma unroll
-  for (int mt = 0; mt < S::DV / 32; ++mt) o[mt] = f32x16{};
+  for (int mt = 0; mt < S::MT; ++mt) o[mt] = f32x16{};
   float m_run = -__builtin_inff();  // running max, log2 domain
   float lsum = 0.f;                 // partial row sum (when not from MFMA)
 
-  const int ntiles = (Lk + kBN - 1) / kBN;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  using Full = std::integral_constant<bool, false>;
+  using Ragged = std::integral_constant<bool, true>;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1, j0 = t * kBN;
-    const bool tail = (j0 + kBN > Lk);
-    if (t + 1 < ntiles) load_tile(j0 + kBN);
+  // Softmax and P.V of one tile whose scores are in (c0, c1); MASK marks the
+  // ragged last tile.
+  auto softmax_tile = [&](auto mask_c, f32x16 &c0, f32x16 &c1, int j0,
+                          const uint16_t *vb) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    softmax_pv<DK, MASK>(c0, j0, Lk, c, m_run, lsum, o, vb, P::VST, lane);
+    if constexpr (NSUB == 2)
+      softmax_pv<DK, MASK>(c1, j0 + 32, Lk, c, m_run, lsum, o, vb + 32, P::VST, lane);
+  };
+  auto scores_tile = [&](const uint16_t *kb, f32x16 &c0, f32x16 &c1) {
+    c0 = scores_subtile<DK>(kb, qf);
+    if constexpr (NSUB == 2) c1 = scores_subtile<DK>(kb + 32 * S::KST, qf);
+  };
 
-    f32x16 s[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) s[nt] = scores_subtile<DK>(&Ks[buf][0], nt * 32, qf, lane);
-    if (tail) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (j0 + nt * 32 + acc_key(i, lane) >= Lk) s[nt][i] = -__builtin_inff();
+  if constexpr (kPipelined) {
+    // Two register sets alternate between the current tile's scores and the
+    // next tile's (the loop is unrolled by two), so nothing is copied.
+    f32x16 sa0, sa1, sb0, sb1;
+    scores_tile(Ks + koff, sa0, sa1);
+    int kb_next = 1;  // LDS K buffer holding tile t+1
+    // Iteration t < ntiles-1: a next tile exists.
+    auto iter = [&](f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1, int t) {
+      const int j0 = t * BN;
+      const bool has_next2 = t + 2 < ntiles;
+      if (has_next2) st.load_k(kr, j0 + 2 * BN, d);
+      st.load_v(vr, j0 + BN, d);
+      scores_tile(Ks + kb_next * P::KBUF + koff, n0, n1);
+      softmax_tile(Full{}, c0, c1, j0, Vt + (t & 1) * P::VBUF + voff);
+      const int kb_next2 = (kb_next == 2) ? 0 : kb_next + 1;
+      if (has_next2) st.store_k(Ks + kb_next2 * P::KBUF);
+      st.store_v(Vt + ((t + 1) & 1) * P::VBUF);
+      __syncthreads();
+      kb_next = kb_next2;
+    };
+    auto last = [&](f32x16 &c0, f32x16 &c1, int t) {
+      const uint16_t *vb = Vt + (t & 1) * P::VBUF + voff;
+      if (ragged) softmax_tile(Ragged{}, c0, c1, t * BN, vb);
+      else softmax_tile(Full{}, c0, c1, t * BN, vb);
+    };
+    int t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+      iter(sa0, sa1, sb0, sb1, t);
+      iter(sb0, sb1, sa0, sa1, t + 1);
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float mt_new = mx * c;
-    if (__any(mt_new > m_run + kRescaleSlack)) {
-      const float mn = fmaxf(m_run, mt_new);
-      const float alpha = fast_exp2(m_run - mn);
-#pragma unroll
-      for (int mt = 0; mt < S::DV / 32; ++mt) o[mt] *= alpha;
-      lsum *= alpha;
-      m_run = mn;
+    if (t + 1 < ntiles) {
+      iter(sa0, sa1, sb0, sb1, t);
+      last(sb0, sb1, t + 1);
+    } else {
+      last(sa0, sa1, t);
     }
-    const float nm = -m_run;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * kk + j;
-          float x = fast_exp2(__builtin_fmaf(s[nt][i], c, nm));
-          if (tail && j0 + nt * 32 + acc_key(i, lane) >= Lk) x = 0.f;
-          p[j] = x;
-          if constexpr (!S::kOnes) lsum += x;
-        }
-        u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-        pv_chunk<DK>(o, &Vt[buf][0], VST, nt * 2 + kk, as_bf16x8(pk), lane);
+  } else {
+    // Double buffering: tile t+1 is staged while tile t is computed; the
+    // loop is unrolled by two so both buffers have fixed LDS addresses.
+    const int nfull = Lk / BN;
+    auto step = [&](auto buf_c, auto mask_c, int t) {
+      constexpr int BUF = decltype(buf_c)::value;
+      const int j0 = t * BN;
+      const bool more = t + 1 < ntiles;
+      if (more) {
+        st.load_k(kr, j0 + BN, d);
+        st.load_v(vr, j0 + BN, d);
       }
+      f32x16 c0, c1;
+      scores_tile(Ks + BUF * P::KBUF + koff, c0, c1);
+      softmax_tile(mask_c, c0, c1, j0, Vt + BUF * P::VBUF + voff);
+      if (more) {
+        st.store_k(Ks + (1 - BUF) * P::KBUF);
+        st.store_v(Vt + (1 - BUF) * P::VBUF);
+      }
+      __syncthreads();
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    int t = 0;
+    for (; t + 2 <= nfull; t += 2) {
+      step(B0{}, Full{}, t);
+      step(B1{}, Full{}, t + 1);
     }
-
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+    if (t < nfull) {
+      step(B0{}, Full{}, t);
+      ++t;
+      if (t < ntiles) step(B1{}, Ragged{}, t);
+    } else if (t < ntiles) {
+      step(B0{}, Ragged{}, t);
+    }
   }
 
   store_out<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
@@ -329,7 +504,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_stream_bf16(Bf16Args a) {
 // Short-key kernel: Lk <= kShortMax, every key resident in LDS.
 
 template <int DK, int NW, int QPW, bool OUT_F32>
-__global__ __launch_bounds__(NW * kWave) void attn_short_bf16(Bf16Args a) {
+__global__ __launch_bounds__(NW * kWave, (min_blocks<DK, NW>()))
+void attn_short_bf16(Bf16Args a) {
   using S = Shape<DK>;
   constexpr int NT = NW * kWave;
   constexpr int NKT = kShortMax / 32;
@@ -342,68 +518,71 @@ __global__ __launch_bounds__(NW * kWave) void attn_short_bf16(Bf16Args a) {
   const int bh = wg / a.qblocks;
   const int qbase = (wg - bh * a.qblocks) * (NW * kQW * QPW);
   const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
-  const uint16_t *qg = a.q + (size_t)bh * Lq * d;
-  const uint16_t *kg = a.k + (size_t)bh * Lk * d;
-  const uint16_t *vg = a.v + (size_t)bh * Lk * d;
   const float c = a.c;
+  const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
+  const rsrc_t kr = make_rsrc(a.k + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  const rsrc_t vr = make_rsrc(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
   const int nkt = (Lk + 31) >> 5;
   const int keys = nkt * 32;
 
   // Issue the first query tile's loads before staging K and V.
   bf16x8 qf[DK / 16];
-  load_q<DK>(qf, qg, qbase + wave * kQW, Lq, d, a.qsign, lane);
+  load_q<DK>(qf, qr, qbase + wave * kQW, d, a.qsign, lane);
 
-  init_k_pad<DK>(Ks, keys, d, tid, NT);
-  init_vt_const<DK>(Vt, VST, keys, d, tid, NT);
+  init_k_pad<DK, kShortMax>(Ks, d, tid, NT);
+  init_vt_const<DK, kShortMax>(Vt, VST, d, tid, NT);
+  // K rows [0, keys): 16-byte chunks, rows past Lk read as zero.
   for (int idx = tid; idx < keys * S::DK8; idx += NT) {
-    const int row = idx / S::DK8, ch = idx % S::DK8;
-    if (ch < d8) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < Lk) x = ld16(kg + (size_t)row * d + ch * 8);
-      st16(&Ks[row * S::KST + ch * 8], x);
-    }
+    const int row = idx / S::DK8, ch = idx - row * S::DK8;
+    if (ch < d8) st16(&Ks[row * S::KST + ch * 8], bload16(kr, (uint32_t)(row * d + ch * 8) * 2u));
   }
+  // V^T: units of 4 keys x 8 columns; groups past keys/4 are idle.
   const int ngroups = keys / 4;
-  for (int u = tid; u < ngroups * d8; u += NT) {
-    const int g = u % ngroups, ch = u / ngroups;
-    u32x4 rows[4];
+  for (int u = tid; u < (kShortMax / 4) * S::DK8; u += NT) {
+    const int g = u & (kShortMax / 4 - 1), ch = u / (kShortMax / 4);
+    if (g < ngroups && ch < d8) {
+      u32x4 rows[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = 4 * g + r;
-      rows[r] = (j < Lk) ? ld16(vg + (size_t)j * d + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+      for (int r = 0; r < 4; ++r)
+        rows[r] = bload16(vr, (uint32_t)((4 * g + r) * d + ch * 8) * 2u);
+      store_vt_unit(Vt, VST, ch * 8, g, rows);
     }
-    store_vt_unit(Vt, VST, ch * 8, g, rows);
   }
   __syncthreads();
+
+  const int koff = (lane & 31) * S::KST + 8 * (lane >> 5);
+  const int voff = (lane & 31) * VST + 8 * (lane >> 5);
 
   for (int t = 0; t < QPW; ++t) {
     const int q0 = qbase + (t * NW + wave) * kQW;
     bf16x8 qn[DK / 16];
-    if (t + 1 < QPW) load_q<DK>(qn, qg, q0 + NW * kQW, Lq, d, a.qsign, lane);
+    if (t + 1 < QPW) load_q<DK>(qn, qr, q0 + NW * kQW, d, a.qsign, lane);
 
     f32x16 s[NKT];
     float mx = -__builtin_inff();
 #pragma unroll
     for (int nt = 0; nt < NKT; ++nt) {
       if (nt < nkt) {
-        s[nt] = scores_subtile<DK>(Ks, nt * 32, qf, lane);
+        s[nt] = scores_subtile<DK>(Ks + koff + nt * 32 * S::KST, qf);
+        if (nt == nkt - 1) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (nt * 32 + acc_key(i, lane) >= Lk) s[nt][i] = -__builtin_inff();
-          mx = fmaxf(mx, s[nt][i]);
+          for (int i = 0; i < 16; ++i)
+            if (nt * 32 + acc_key(i, lane) >= Lk) s[nt][i] = -__builtin_inff();
         }
+        mx = max16(s[nt], mx);
       }
     }
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = max_halves(mx);
     const float nm = -(mx * c);
 
-    f32x16 o[S::DV / 32];
+    f32x16 o[S::MT];
 #pragma unroll
-    for (int mt = 0; mt < S::DV / 32; ++mt) o[mt] = f32x16{};
+    for (int mt = 0; mt < S::MT; ++mt) o[mt] = f32x16{};
     float lsum = 0.f;
 #pragma unroll
     for (int nt = 0; nt < NKT; ++nt) {
       if (nt < nkt) {
+        const bool last = (nt == nkt - 1);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           float p[8];
@@ -411,13 +590,13 @@ __global__ __launch_bounds__(NW * kWave) void attn_short_bf16(Bf16Args a) {
           for (int j = 0; j < 8; ++j) {
             const int i = 8 * kk + j;
             float x = fast_exp2(__builtin_fmaf(s[nt][i], c, nm));
-            if (nt * 32 + acc_key(i, lane) >= Lk) x = 0.f;
+            if (last && nt * 32 + acc_key(i, lane) >= Lk) x = 0.f;
             p[j] = x;
             if constexpr (!S::kOnes) lsum += x;
           }
-          u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-          pv_chunk<DK>(o, Vt, VST, nt * 2 + kk, as_bf16x8(pk), lane);
+          const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+          pv_chunk<DK>(o, Vt + voff + (nt * 2 + kk) * 16, VST, as_bf16x8(pk));
         }
       }
     }
@@ -429,9 +608,19 @@ __global__ __launch_bounds__(NW * kWave) void attn_short_bf16(Bf16Args a) {
   }
 }
 
-constexpr int kStreamWaves = 4;
-constexpr int kShortWaves = 4;
-constexpr int kShortTiles = 2;   // query tiles per wave in the short kernel
+// Launch shapes (build-time knobs for tuning; the defaults are the tuned ones).
+#ifndef SDATTN_STREAM_WAVES
+#define SDATTN_STREAM_WAVES 4
+#endif
+#ifndef SDATTN_SHORT_WAVES
+#define SDATTN_SHORT_WAVES 4
+#endif
+#ifndef SDATTN_SHORT_TILES
+#define SDATTN_SHORT_TILES 1
+#endif
+constexpr int kStreamWaves = SDATTN_STREAM_WAVES;
+constexpr int kShortWaves = SDATTN_SHORT_WAVES;
+constexpr int kShortTiles = SDATTN_SHORT_TILES;   // query tiles per wave (short kernel)
 
 template <int DK>
 hipError_t launch_dk(const Bf16Args &base, int BH, bool short_path, bool out_f32,

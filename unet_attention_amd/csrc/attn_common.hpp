@@ -76,9 +76,35 @@ __device__ __forceinline__ void st16(void *p, u32x4 x) {
   *reinterpret_cast<u32x4 *>(p) = x;
 }
 
-// Exchange a value with the lane 32 positions away (the other half-wave).
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32);
+// Half-wave exchanges through v_permlane32_swap (a VALU op, no LDS trip).
+// With both operands holding x, the swap leaves {x_lo, x_lo} in the first
+// result and {x_hi, x_hi} in the second, lane by lane.
+__device__ __forceinline__ void halves(float x, float &lo_bcast, float &hi_bcast) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  lo_bcast = __uint_as_float(r[0]);
+  hi_bcast = __uint_as_float(r[1]);
+}
+
+// max over lanes l and l ^ 32.
+__device__ __forceinline__ float max_halves(float x) {
+  float a, b;
+  halves(x, a, b);
+  return fmaxf(a, b);
+}
+
+// sum over lanes l and l ^ 32.
+__device__ __forceinline__ float sum_halves(float x) {
+  float a, b;
+  halves(x, a, b);
+  return a + b;
+}
+
+// Every lane gets the value of lane (l % 32).
+__device__ __forceinline__ float from_low_half(float x) {
+  float a, b;
+  halves(x, a, b);
+  return a;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) {
