@@ -501,7 +501,569 @@ void attn_stream_bf16(Bf16Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Streaming kernel, DMA form (default): K and V tiles go from HBM straight
+// into LDS with buffer->LDS transfers, so no registers, LDS writes or vector
+// instructions are spent on staging, and three LDS buffers let the transfer
+// of tile t+2 overlap the computation of tile t.
+//
+// K keeps its row-major [key][DK+8] layout (the MFMA A operand of S^T is a
+// plain 16-byte LDS read).  V is also kept row-major, [key][VSTR], and the A
+// operand of O^T += V^T P^T is assembled by two transposing LDS reads
+// (ds_read_b64_tr_b16): within each 16-lane group, output lane i, element j
+// is element (i % 4) of the 8 bytes addressed by source lane 4*j + i/4.  With
+// source lane 4*j + q of group g pointing at V[key0 + 4*(g/2) + j][16*(g%2) +
+// 4*q], lane l receives row (l % 32) of V^T for keys key0 + 4*(l/32) + 0..3,
+// and the second read (8 rows further) keys key0 + 8 + 4*(l/32) + 0..3:
+// exactly the key order of the S^T accumulator registers.  Columns [d, DV)
+// of every V row are constants written once (a column of ones at d when the
+// row sum comes from the matrix core, zeros otherwise); the transfers skip
+// them.
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 16-byte buffer -> LDS transfer for every active lane: lane i writes
+// lds + 16*i bytes (lds is wave-uniform); offsets at or past the buffer size
+// write zeros.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint16_t *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ s16x4 ld_tr16(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<uint16_t *>(p));
+}
+
+// Wait until at most N of this wave's buffer loads are in flight and all of
+// its LDS operations are done, then synchronise the workgroup.  (A plain
+// __syncthreads would wait for every load, including the prefetch of the
+// tile after next.)
+template <int N>
+__device__ __forceinline__ void vmcnt_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Same with a run-time count n in [0, MAXN] (wave-uniform).
+template <int MAXN>
+__device__ __forceinline__ void vmcnt_barrier_rt(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      vmcnt_barrier<MAXN>();
+      return;
+    }
+    vmcnt_barrier_rt<MAXN - 1>(n);
+  } else {
+    vmcnt_barrier<0>();
+  }
+}
+
+// V row stride of the DMA kernel: an odd multiple of 64 bytes, so the four
+// key rows one transposing read touches fall on distinct LDS banks.
+template <int DK>
+constexpr int dma_vstr() {
+  return ((Shape<DK>::DV * 2) % 128 == 0) ? Shape<DK>::DV + 32 : Shape<DK>::DV;
+}
+// 64-key tiles when three K and three V buffers fit in the CU's 160 KB.
+template <int DK>
+constexpr int dma_bn() {
+  return 3 * 64 * (Shape<DK>::KST + dma_vstr<DK>()) * 2 <= 160 * 1024 ? 64 : 32;
+}
+
+template <int DK, int NW>
+struct DmaPlan {
+  using S = Shape<DK>;
+  static constexpr int BN = dma_bn<DK>();
+  static constexpr int NSUB = BN / 32;
+  static constexpr int NB = 3;                      // LDS buffers per operand
+  static constexpr int KCR = S::KST / 8;            // 16-byte chunks per K row
+  static constexpr int VSTR = dma_vstr<DK>();
+  static constexpr int VCR = VSTR / 8;
+  static constexpr int KBUF = BN * S::KST;          // elements per K buffer
+  static constexpr int VBUF = BN * VSTR;            // elements per V buffer
+  static constexpr int KI = (BN * KCR + 63) / 64;   // transfers (64 lanes) per K tile
+  static constexpr int VI = (BN * VCR + 63) / 64;   // ... per V tile
+  static constexpr int NI = KI + VI;
+  static constexpr int NIW = (NI + NW - 1) / NW;    // per wave, upper bound
+};
+
+template <int DK, int NW, bool OUT_F32>
+__global__ __launch_bounds__(NW * kWave, (min_blocks<DK, NW>()))
+void attn_stream_dma_bf16(Bf16Args a) {
+  using S = Shape<DK>;
+  using P = DmaPlan<DK, NW>;
+  constexpr int BN = P::BN, NSUB = P::NSUB;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[P::NB * (P::KBUF + P::VBUF)];
+  uint16_t *const Ks = smem;
+  uint16_t *const Vs = smem + P::NB * P::KBUF;
+
+  // The wave index is uniform: keep it (and everything derived from it, such
+  // as the LDS destinations of the transfers) in scalar registers.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = xcd_remap(blockIdx.x, a.nwg);
+  const int bh = wg / a.qblocks;
+  const int q0 = (wg - bh * a.qblocks) * (NW * kQW) + wave * kQW;
+  const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
+  const float c = a.c;
+  const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
+  const rsrc_t kr = make_rsrc(a.k + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  const rsrc_t vr = make_rsrc(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  const int ntiles = (Lk + BN - 1) / BN;
+  const bool ragged = (Lk % BN) != 0;
+
+  // This wave's share of each tile's transfers: instruction i = wave + NW*r
+  // covers 64 consecutive 16-byte chunks of the K (i < KI) or V buffer.
+  uint32_t goff[P::NIW];  // source byte offset within a tile
+  int loff[P::NIW];       // destination element offset within a buffer
+  bool isk[P::NIW], act[P::NIW];
+#pragma unroll
+  for (int r = 0; r < P::NIW; ++r) {
+    const int i = wave + NW * r;
+    isk[r] = i < P::KI;
+    const int blk = isk[r] ? i : i - P::KI;
+    const int cpos = blk * 64 + lane;
+    const int cr = isk[r] ? P::KCR : P::VCR;
+    const int row = cpos / cr, col = cpos - row * cr;
+    act[r] = (i < P::NI) && row < BN && col < d8;
+    goff[r] = (uint32_t)(row * d + col * 8) * 2u;
+    loff[r] = blk * 512;
+  }
+  // Transfers this wave really issues per tile (one with no active lane is
+  // branched over and does not count towards vmcnt).
+  int my_count = 0;
+#pragma unroll
+  for (int r = 0; r < P::NIW; ++r)
+    if (wave + NW * r < P::NI && __any(act[r])) ++my_count;
+  auto issue = [&](int tt, int b) {
+    const uint32_t toff = (uint32_t)(tt * BN * d) * 2u;
+#pragma unroll
+    for (int r = 0; r < P::NIW; ++r) {
+      if (wave + NW * r < P::NI) {
+        if (isk[r]) {
+          if (act[r]) dma16(kr, toff + goff[r], Ks + b * P::KBUF + loff[r]);
+        } else {
+          if (act[r]) dma16(vr, toff + goff[r], Vs + b * P::VBUF + loff[r]);
+        }
+      }
+    }
+  };
+
+  bf16x8 qf[DK / 16];
+  load_q<DK>(qf, qr, q0, d, a.qsign, lane);
+  issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
+
+  // Constant columns, never touched by the transfers: K columns [d, DK) and
+  // V columns [d, DV) (ones at d for the matrix-core row sum).
+  if (d8 < S::DK8) {
+    for (int r = tid; r < P::NB * BN; r += NW * kWave)
+      st16(Ks + r * S::KST + d8 * 8, u32x4{0u, 0u, 0u, 0u});
+  }
+  for (int idx = tid; idx < P::NB * BN * (S::DV / 8); idx += NW * kWave) {
+    const int r = idx / (S::DV / 8), c8 = idx - r * (S::DV / 8);
+    if (c8 >= d8) {
+      const uint32_t w0 = (S::kOnes && c8 == d8) ? uint32_t(kBf16One) : 0u;
+      st16(Vs + r * P::VSTR + c8 * 8, u32x4{w0, 0u, 0u, 0u});
+    }
+  }
+
+  // Per-lane LDS read bases: K rows (l % 32); V rows for the transposing reads.
+  const int koff = (lane & 31) * S::KST + 8 * (lane >> 5);
+  const int g = lane >> 4, pl = lane & 15;
+  const int voff = (4 * (g >> 1) + (pl >> 2)) * P::VSTR + 16 * (g & 1) + 4 * (pl & 3);
+
+  f32x16 o[S::MT];
+#pragma unroll
+  for (int mt = 0; mt < S::MT; ++mt) o[mt] = f32x16{};
+  float m_run = -__builtin_inff();
+  float lsum = 0.f;
+
+  // O^T += V^T P^T for one 16-key chunk, V^T assembled by transposing reads.
+  auto pv = [&](const uint16_t *vb, int kc, bf16x8 pk) {
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt) {
+      const uint16_t *vp = vb + voff + kc * 16 * P::VSTR + mt * 32;
+      const s16x4 lo = ld_tr16(vp), hi = ld_tr16(vp + 8 * P::VSTR);
+      const bf16x8 av =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[mt] = mfma32x32x16(av, pk, o[mt]);
+    }
+  };
+
+  // Softmax update for one 32-key sub-tile (scores s, first key key0), then
+  // its two P.V chunks from V buffer vb.
+  auto sub = [&](auto mask_c, f32x16 &s, int key0, const uint16_t *vb, int kc0) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + acc_key(i, lane) >= Lk) s[i] = -__builtin_inff();
+    }
+    float mx = max16(s, -__builtin_inff());
+    mx = max_halves(mx);
+    const float mt_new = mx * c;
+    if (__any(mt_new > m_run + kRescaleSlack)) {
+      const float mn = fmaxf(m_run, mt_new);
+      const float alpha = fast_exp2(m_run - mn);
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt) o[mt] *= alpha;
+      lsum *= alpha;
+      m_run = mn;
+    }
+    const float nm = -m_run;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 8 * kk + j;
+        float x = fast_exp2(__builtin_fmaf(s[i], c, nm));
+        if constexpr (MASK) {
+          if (key0 + acc_key(i, lane) >= Lk) x = 0.f;
+        }
+        p[j] = x;
+        if constexpr (!S::kOnes) lsum += x;
+      }
+      const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+      pv(vb, kc0 + kk, as_bf16x8(pk));
+    }
+  };
+
+  using Full = std::integral_constant<bool, false>;
+  using Ragged = std::integral_constant<bool, true>;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+
+  // Tile t, held in LDS buffer B (= t % 3, a compile-time constant): start
+  // the transfer of tile t+2 into buffer (B+2) % 3, compute tile t, then wait
+  // until tile t+1 has landed everywhere (tile t+2 may stay in flight).
+  auto step = [&](auto b_c, auto mask_c, int t) {
+    constexpr int B = decltype(b_c)::value;
+    if (t + 2 < ntiles) issue(t + 2, (B + 2) % 3);
+    const uint16_t *kb = Ks + B * P::KBUF + koff;
+    const uint16_t *vb = Vs + B * P::VBUF;
+    f32x16 s0 = scores_subtile<DK>(kb, qf), s1;
+    if constexpr (NSUB == 2) s1 = scores_subtile<DK>(kb + 32 * S::KST, qf);
+    sub(mask_c, s0, t * BN, vb, 0);
+    if constexpr (NSUB == 2) sub(mask_c, s1, t * BN + 32, vb, 2);
+    if (t + 1 < ntiles) vmcnt_barrier_rt<P::NIW>(t + 2 < ntiles ? my_count : 0);
+  };
+
+  // Tile 0 (and the constants) must have landed before anyone reads them;
+  // tile 1's transfers may still be in flight.
+  vmcnt_barrier_rt<P::NIW>(ntiles > 1 ? my_count : 0);
+
+  const int nfull = ragged ? ntiles - 1 : ntiles;
+  int t = 0;
+  for (; t + 3 <= nfull; t += 3) {
+    step(B0{}, Full{}, t);
+    step(B1{}, Full{}, t + 1);
+    step(B2{}, Full{}, t + 2);
+  }
+  if (t < nfull) {
+    step(B0{}, Full{}, t);
+    if (t + 1 < nfull) {
+      step(B1{}, Full{}, t + 1);
+      if (ragged) step(B2{}, Ragged{}, t + 2);
+    } else if (ragged) {
+      step(B1{}, Ragged{}, t + 1);
+    }
+  } else if (ragged) {
+    step(B0{}, Ragged{}, t);
+  }
+
+  store_out<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming kernel, ping-pong form.  A workgroup is eight waves (two per
+// SIMD, 256 query rows).  Each wave alternates two phases per key tile:
+//   M_t: S_t = K_t Q^T and O^T += V_{t-1}^T P_{t-1}^T  (matrix cores)
+//   V_t: online softmax of S_t -> P_t (bf16)           (vector ALUs)
+// Waves 0-3 ("A") run phase h in half-period h, waves 4-7 ("B") run phase
+// h-1, with a workgroup barrier between half-periods, so on every SIMD one
+// wave issues matrix instructions while the other does the softmax: on
+// MI355X a VALU-only wave overlaps an MFMA-only wave on the same SIMD far
+// better than the two instruction kinds overlap within one wave.  K/V tiles
+// arrive by buffer->LDS transfers two tiles ahead in four LDS buffers; the
+// ragged last tile (if any) is computed after the loop by all waves at once.
+
+template <int DK>
+constexpr int pp_bn() {
+  // 64-key tiles need two score accumulators per wave: above 128 columns
+  // they no longer fit the 256 VGPRs beside the O accumulators.
+  return DK <= 128 && 4 * 64 * (Shape<DK>::KST + dma_vstr<DK>()) * 2 <= 160 * 1024 ? 64 : 32;
+}
+
+template <int DK>
+struct PPPlan {
+  using S = Shape<DK>;
+  static constexpr int NW = 8;
+  static constexpr int BN = pp_bn<DK>();
+  static constexpr int NSUB = BN / 32;
+  static constexpr int NB = 4;
+  static constexpr int KCR = S::KST / 8;
+  static constexpr int VSTR = dma_vstr<DK>();
+  static constexpr int VCR = VSTR / 8;
+  static constexpr int KBUF = BN * S::KST;
+  static constexpr int VBUF = BN * VSTR;
+  static constexpr int KI = (BN * KCR + 63) / 64;
+  static constexpr int VI = (BN * VCR + 63) / 64;
+  static constexpr int NI = KI + VI;
+  static constexpr int NIW = (NI + NW - 1) / NW;
+};
+
+template <int DK, bool OUT_F32>
+__global__ __launch_bounds__(8 * kWave, 1)
+void attn_stream_pp_bf16(Bf16Args a) {
+  using S = Shape<DK>;
+  using P = PPPlan<DK>;
+  constexpr int NW = P::NW, BN = P::BN, NSUB = P::NSUB;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[P::NB * (P::KBUF + P::VBUF)];
+  uint16_t *const Ks = smem;
+  uint16_t *const Vs = smem + P::NB * P::KBUF;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: leads by half a period, 1: lags
+  const int wg = xcd_remap(blockIdx.x, a.nwg);
+  const int bh = wg / a.qblocks;
+  const int q0 = (wg - bh * a.qblocks) * (NW * kQW) + wave * kQW;
+  const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
+  const float c = a.c;
+  const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
+  const rsrc_t kr = make_rsrc(a.k + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  const rsrc_t vr = make_rsrc(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  const int ntiles = (Lk + BN - 1) / BN;
+  const int nfull = Lk / BN;
+
+  // Transfers: instruction i = wave + NW*r covers 64 consecutive 16-byte
+  // chunks of a K (i < KI) or V buffer.
+  uint32_t goff[P::NIW];
+  int loff[P::NIW];
+  bool isk[P::NIW], act[P::NIW];
+#pragma unroll
+  for (int r = 0; r < P::NIW; ++r) {
+    const int i = wave + NW * r;
+    isk[r] = i < P::KI;
+    const int blk = isk[r] ? i : i - P::KI;
+    const int cpos = blk * 64 + lane;
+    const int cr = isk[r] ? P::KCR : P::VCR;
+    const int row = cpos / cr, col = cpos - row * cr;
+    act[r] = (i < P::NI) && row < BN && col < d8;
+    goff[r] = (uint32_t)(row * d + col * 8) * 2u;
+    loff[r] = blk * 512;
+  }
+  int my_count = 0;
+#pragma unroll
+  for (int r = 0; r < P::NIW; ++r)
+    if (wave + NW * r < P::NI && __any(act[r])) ++my_count;
+  auto issue = [&](int tt) {
+    const int b = tt & 3;
+    const uint32_t toff = (uint32_t)(tt * BN * d) * 2u;
+#pragma unroll
+    for (int r = 0; r < P::NIW; ++r) {
+      if (wave + NW * r < P::NI) {
+        if (isk[r]) {
+          if (act[r]) dma16(kr, toff + goff[r], Ks + b * P::KBUF + loff[r]);
+        } else {
+          if (act[r]) dma16(vr, toff + goff[r], Vs + b * P::VBUF + loff[r]);
+        }
+      }
+    }
+  };
+
+  bf16x8 qf[DK / 16];
+  load_q<DK>(qf, qr, q0, d, a.qsign, lane);
+  issue(0);
+  if (ntiles > 1) issue(1);
+  if (d8 < S::DK8) {
+    for (int r = tid; r < P::NB * BN; r += NW * kWave)
+      st16(Ks + r * S::KST + d8 * 8, u32x4{0u, 0u, 0u, 0u});
+  }
+  for (int idx = tid; idx < P::NB * BN * (S::DV / 8); idx += NW * kWave) {
+    const int r = idx / (S::DV / 8), c8 = idx - r * (S::DV / 8);
+    if (c8 >= d8) {
+      const uint32_t w0 = (S::kOnes && c8 == d8) ? uint32_t(kBf16One) : 0u;
+      st16(Vs + r * P::VSTR + c8 * 8, u32x4{w0, 0u, 0u, 0u});
+    }
+  }
+
+  const int koff = (lane & 31) * S::KST + 8 * (lane >> 5);
+  const int gq = lane >> 4, pl = lane & 15;
+  const int voff = (4 * (gq >> 1) + (pl >> 2)) * P::VSTR + 16 * (gq & 1) + 4 * (pl & 3);
+
+  f32x16 o[S::MT];
+#pragma unroll
+  for (int mt = 0; mt < S::MT; ++mt) o[mt] = f32x16{};
+  float m_run = -__builtin_inff();
+  float lsum = 0.f;
+  f32x16 s0, s1;        // scores of the tile whose softmax comes next
+  u32x4 pk[2 * NSUB];   // bf16 weights of the tile whose P.V comes next
+
+  auto scores = [&](int t) {
+    const uint16_t *kb = Ks + (t & 3) * P::KBUF + koff;
+    s0 = scores_subtile<DK>(kb, qf);
+    if constexpr (NSUB == 2) s1 = scores_subtile<DK>(kb + 32 * S::KST, qf);
+  };
+  auto pv = [&](int t) {
+    const uint16_t *vb = Vs + (t & 3) * P::VBUF + voff;
+#pragma unroll
+    for (int kc = 0; kc < 2 * NSUB; ++kc) {
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt) {
+        const uint16_t *vp = vb + kc * 16 * P::VSTR + mt * 32;
+        const s16x4 lo = ld_tr16(vp), hi = ld_tr16(vp + 8 * P::VSTR);
+        const bf16x8 av =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[mt] = mfma32x32x16(av, as_bf16x8(pk[kc]), o[mt]);
+      }
+    }
+  };
+  // Softmax of one key tile into weights pk[0 .. 2*NSUB-1].  One maximum
+  // over the whole tile decides the rescale before any weight is formed:
+  // P.V of this tile runs in a later phase, so weights formed under a
+  // maximum that is raised afterwards would never be corrected.
+  auto soft_tile = [&](auto mask_c, int key0) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (key0 + acc_key(i, lane) >= Lk) s0[i] = -__builtin_inff();
+        if constexpr (NSUB == 2)
+          if (key0 + 32 + acc_key(i, lane) >= Lk) s1[i] = -__builtin_inff();
+      }
+    }
+    float mx = max16(s0, -__builtin_inff());
+    if constexpr (NSUB == 2) mx = max16(s1, mx);
+    mx = max_halves(mx);
+    const float mt_new = mx * c;
+    if (__any(mt_new > m_run + kRescaleSlack)) {
+      const float mn = fmaxf(m_run, mt_new);
+      const float alpha = fast_exp2(m_run - mn);
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt) o[mt] *= alpha;
+      lsum *= alpha;
+      m_run = mn;
+    }
+    const float nm = -m_run;
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) {
+      const f32x16 &sv = u == 0 ? s0 : s1;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float pv8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * kk + j;
+          float x = fast_exp2(__builtin_fmaf(sv[i], c, nm));
+          if constexpr (MASK) {
+            if (key0 + 32 * u + acc_key(i, lane) >= Lk) x = 0.f;
+          }
+          pv8[j] = x;
+          if constexpr (!S::kOnes) lsum += x;
+        }
+        pk[2 * u + kk] = u32x4{pack_bf16x2(pv8[0], pv8[1]), pack_bf16x2(pv8[2], pv8[3]),
+                               pack_bf16x2(pv8[4], pv8[5]), pack_bf16x2(pv8[6], pv8[7])};
+      }
+    }
+  };
+  using Full = std::integral_constant<bool, false>;
+  using Ragged = std::integral_constant<bool, true>;
+
+  // Tile 0 must have landed; tile 1 may still be in flight.
+  vmcnt_barrier_rt<P::NIW>(ntiles > 1 ? my_count : 0);
+
+  const int n = nfull;
+  for (int h = 0; h < 2 * n + 2; ++h) {
+    if ((h & 1) == 0 && (h >> 1) + 2 < ntiles) issue((h >> 1) + 2);
+    const int ph = h - grp;
+    if (ph >= 0) {
+      const int t = ph >> 1;
+      if ((ph & 1) == 0) {
+        __builtin_amdgcn_s_setprio(1);
+        if (t < n) scores(t);
+        if (t >= 1 && t <= n) pv(t - 1);
+        __builtin_amdgcn_s_setprio(0);
+      } else if (t < n) {
+        soft_tile(Full{}, t * BN);
+      }
+    }
+    // Entering half-period h+1; if it starts tile (h+1)/2's matrix phase,
+    // that tile must have landed (the next one may still be in flight).
+    const int tn = (h + 1) >> 1;
+    if (((h + 1) & 1) == 0 && tn < ntiles)
+      vmcnt_barrier_rt<P::NIW>(tn + 1 < ntiles ? my_count : 0);
+    else
+      vmcnt_barrier<0>();
+  }
+
+  if (nfull < ntiles) {
+    // Ragged last tile, all waves together (its transfer has landed: the
+    // loop's barrier entering half-period 2*nfull waited for it).
+    scores(nfull);
+    soft_tile(Ragged{}, nfull * BN);
+    pv(nfull);
+  }
+
+  store_out<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
+}
+
+// ---------------------------------------------------------------------------
 // Short-key kernel: Lk <= kShortMax, every key resident in LDS.
+
+// Epilogue through LDS: the wave writes its normalised 32 x d tile into a
+// private LDS region laid out exactly like the rows in HBM, then stores it
+// with 16-byte contiguous chunks (whole cache lines per instruction).
+template <int DK, bool OUT_F32>
+__device__ __forceinline__ void store_out_staged(const f32x16 (&o)[Shape<DK>::MT],
+                                                 float lsum, void *outp, size_t obase,
+                                                 int q0, int Lq, int d, int lane,
+                                                 uint8_t *stage) {
+  using S = Shape<DK>;
+  constexpr int ELT = OUT_F32 ? 4 : 2;
+  float l;
+  if constexpr (S::kOnes) {
+    float lv = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        if (mt * 32 + 8 * g4 == d) lv = o[mt][4 * g4];
+    l = from_low_half(lv);
+  } else {
+    l = sum_halves(lsum);
+  }
+  const float inv = 1.0f / l;
+  const int r = lane & 31, hb = 4 * (lane >> 5);
+#pragma unroll
+  for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int c0 = mt * 32 + 8 * g4 + hb;
+      if (c0 < d) {
+        const float x0 = o[mt][4 * g4 + 0] * inv, x1 = o[mt][4 * g4 + 1] * inv;
+        const float x2 = o[mt][4 * g4 + 2] * inv, x3 = o[mt][4 * g4 + 3] * inv;
+        uint8_t *dst = stage + (r * d + c0) * ELT;
+        if constexpr (OUT_F32) {
+          *reinterpret_cast<f32x4 *>(dst) = f32x4{x0, x1, x2, x3};
+        } else {
+          *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        }
+      }
+    }
+  // LDS operations of one wave complete in order, so the reads below see the
+  // writes above.
+  const int rows = min(kQW, Lq - q0);
+  if (rows <= 0) return;
+  const int nchunks = rows * d * ELT / 16;
+  uint8_t *gdst = static_cast<uint8_t *>(outp) + (obase + (size_t)q0 * d) * ELT;
+  for (int ch = lane; ch < nchunks; ch += kWave)
+    *reinterpret_cast<u32x4 *>(gdst + (size_t)ch * 16) =
+        *reinterpret_cast<const u32x4 *>(stage + ch * 16);
+}
 
 template <int DK, int NW, int QPW, bool OUT_F32>
 __global__ __launch_bounds__(NW * kWave, (min_blocks<DK, NW>()))
@@ -510,8 +1072,16 @@ void attn_short_bf16(Bf16Args a) {
   constexpr int NT = NW * kWave;
   constexpr int NKT = kShortMax / 32;
   constexpr int VST = kShortMax + 8;
+  constexpr int KCH = (kShortMax * S::DK8 + NT - 1) / NT;        // K chunks / thread
+  constexpr int VCH = ((kShortMax / 4) * S::DK8 + NT - 1) / NT;  // V units / thread
+  constexpr int STAGE = kQW * DK * (OUT_F32 ? 4 : 2);            // bytes per wave
+  // Output staging only where K, V^T and the staging area fit in half of the
+  // CU's LDS (two workgroups per CU); otherwise rows are stored directly.
+  constexpr int KV_BYTES = (kShortMax * S::KST + S::DV * VST) * 2;
+  constexpr bool kStaged = KV_BYTES + NW * STAGE <= 80 * 1024;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kShortMax * S::KST];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[S::DV * VST];
+  __shared__ __attribute__((aligned(16))) uint8_t Ost[kStaged ? NW * STAGE : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = xcd_remap(blockIdx.x, a.nwg);
@@ -524,34 +1094,50 @@ void attn_short_bf16(Bf16Args a) {
   const rsrc_t vr = make_rsrc(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
   const int nkt = (Lk + 31) >> 5;
   const int keys = nkt * 32;
+  const int ngroups = keys / 4;
 
-  // Issue the first query tile's loads before staging K and V.
+  // Issue every HBM load first (this wave's first Q tile, all of K, all of
+  // V), so their latencies overlap; only then write LDS.
   bf16x8 qf[DK / 16];
   load_q<DK>(qf, qr, qbase + wave * kQW, d, a.qsign, lane);
+  u32x4 kreg[KCH];
+  u32x4 vreg[VCH][4];
+#pragma unroll
+  for (int t = 0; t < KCH; ++t) {
+    const int idx = tid + t * NT;
+    const int row = idx / S::DK8, ch = idx - row * S::DK8;
+    if (row < keys && ch < d8) kreg[t] = bload16(kr, (uint32_t)(row * d + ch * 8) * 2u);
+  }
+#pragma unroll
+  for (int t = 0; t < VCH; ++t) {
+    const int u = tid + t * NT;
+    const int g = u % (kShortMax / 4), ch = u / (kShortMax / 4);
+    if (g < ngroups && ch < d8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vreg[t][r] = bload16(vr, (uint32_t)((4 * g + r) * d + ch * 8) * 2u);
+    }
+  }
 
   init_k_pad<DK, kShortMax>(Ks, d, tid, NT);
   init_vt_const<DK, kShortMax>(Vt, VST, d, tid, NT);
-  // K rows [0, keys): 16-byte chunks, rows past Lk read as zero.
-  for (int idx = tid; idx < keys * S::DK8; idx += NT) {
-    const int row = idx / S::DK8, ch = idx - row * S::DK8;
-    if (ch < d8) st16(&Ks[row * S::KST + ch * 8], bload16(kr, (uint32_t)(row * d + ch * 8) * 2u));
-  }
-  // V^T: units of 4 keys x 8 columns; groups past keys/4 are idle.
-  const int ngroups = keys / 4;
-  for (int u = tid; u < (kShortMax / 4) * S::DK8; u += NT) {
-    const int g = u & (kShortMax / 4 - 1), ch = u / (kShortMax / 4);
-    if (g < ngroups && ch < d8) {
-      u32x4 rows[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        rows[r] = bload16(vr, (uint32_t)((4 * g + r) * d + ch * 8) * 2u);
-      store_vt_unit(Vt, VST, ch * 8, g, rows);
-    }
+  for (int t = 0; t < KCH; ++t) {
+    const int idx = tid + t * NT;
+    const int row = idx / S::DK8, ch = idx - row * S::DK8;
+    if (row < keys && ch < d8) st16(&Ks[row * S::KST + ch * 8], kreg[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < VCH; ++t) {
+    const int u = tid + t * NT;
+    const int g = u % (kShortMax / 4), ch = u / (kShortMax / 4);
+    if (g < ngroups && ch < d8) store_vt_unit(Vt, VST, ch * 8, g, vreg[t]);
   }
   __syncthreads();
 
   const int koff = (lane & 31) * S::KST + 8 * (lane >> 5);
   const int voff = (lane & 31) * VST + 8 * (lane >> 5);
+  uint8_t *stage = Ost + (kStaged ? wave * STAGE : 0);
 
   for (int t = 0; t < QPW; ++t) {
     const int q0 = qbase + (t * NW + wave) * kQW;
@@ -585,6 +1171,7 @@ void attn_short_bf16(Bf16Args a) {
         const bool last = (nt == nkt - 1);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
+          if (kk == 1 && nt * 32 + 16 >= Lk) break;  // chunk entirely past Lk
           float p[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -600,7 +1187,11 @@ void attn_short_bf16(Bf16Args a) {
         }
       }
     }
-    store_out<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
+    if constexpr (kStaged)
+      store_out_staged<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane,
+                                    stage);
+    else
+      store_out<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
     if (t + 1 < QPW) {
 #pragma unroll
       for (int dk = 0; dk < DK / 16; ++dk) qf[dk] = qn[dk];
@@ -618,7 +1209,15 @@ void attn_short_bf16(Bf16Args a) {
 #ifndef SDATTN_SHORT_TILES
 #define SDATTN_SHORT_TILES 1
 #endif
+#ifndef SDATTN_STREAM_DMA
+#define SDATTN_STREAM_DMA 1
+#endif
+#ifndef SDATTN_STREAM_PINGPONG
+#define SDATTN_STREAM_PINGPONG 0
+#endif
+constexpr bool kStreamPingPong = SDATTN_STREAM_PINGPONG != 0;
 constexpr int kStreamWaves = SDATTN_STREAM_WAVES;
+constexpr bool kStreamDma = SDATTN_STREAM_DMA != 0;
 constexpr int kShortWaves = SDATTN_SHORT_WAVES;
 constexpr int kShortTiles = SDATTN_SHORT_TILES;   // query tiles per wave (short kernel)
 
@@ -636,16 +1235,35 @@ hipError_t launch_dk(const Bf16Args &base, int BH, bool short_path, bool out_f32
     else
       hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, false>),
                          dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
+  } else if (kStreamPingPong && DK <= 160) {
+    const int per_wg = 8 * kQW;
+    a.qblocks = (a.Lq + per_wg - 1) / per_wg;
+    a.nwg = BH * a.qblocks;
+    if (out_f32)
+      hipLaunchKernelGGL((attn_stream_pp_bf16<DK, true>), dim3(a.nwg), dim3(8 * kWave), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((attn_stream_pp_bf16<DK, false>), dim3(a.nwg), dim3(8 * kWave), 0,
+                         stream, a);
   } else {
     const int per_wg = kStreamWaves * kQW;
     a.qblocks = (a.Lq + per_wg - 1) / per_wg;
     a.nwg = BH * a.qblocks;
-    if (out_f32)
-      hipLaunchKernelGGL((attn_stream_bf16<DK, kStreamWaves, true>),
-                         dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_stream_bf16<DK, kStreamWaves, false>),
-                         dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
+    if constexpr (kStreamDma) {
+      if (out_f32)
+        hipLaunchKernelGGL((attn_stream_dma_bf16<DK, kStreamWaves, true>),
+                           dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_stream_dma_bf16<DK, kStreamWaves, false>),
+                           dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
+    } else {
+      if (out_f32)
+        hipLaunchKernelGGL((attn_stream_bf16<DK, kStreamWaves, true>),
+                           dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_stream_bf16<DK, kStreamWaves, false>),
+                           dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
+    }
   }
   return hipGetLastError();
 }
