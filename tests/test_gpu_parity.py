@@ -101,7 +101,7 @@ def test_workload5_sampled(dev):
 
 SHAPES = [(1, 1), (15, 2), (33, 63), (65, 64), (129, 65), (17, 77), (40, 127),
           (64, 128), (31, 129), (100, 200), (70, 333)]
-DIMS = [8, 40, 64, 80, 136, 160, 256]
+DIMS = [8, 24, 40, 64, 80, 136, 160, 256]
 
 
 @pytest.mark.parametrize("d", DIMS)
@@ -231,6 +231,55 @@ def test_shifted_keys_stress_running_max(dev):
     tq, tk, tv = tensors_from_f32(q, k, v, "bf16")
     say("shifted keys")
     assert_bf16_gate(run("auto", tq, tk, tv, 0.125, torch.float32), want, "shifted keys")
+
+
+def _aligned_key_case(d, seed, v_big=None):
+    """Every query close to one direction u (|q| ~ 6); key 250 = 24 u, the
+    other keys small: key 250 scores ~144 above the rest (times scale)."""
+    from workloads import bf16_bits_to_f32, round_to_bf16_bits
+    Lq, Lk, jstar = 70, 333, 250
+    u = np.full(d, 1.0 / math.sqrt(d), dtype=np.float32)
+    q = 6.0 * u + _rand((1, 2, Lq, d), seed, 0.3)
+    k = _rand((1, 2, Lk, d), seed + 1, 0.5)
+    k[:, :, jstar] = 24.0 * u
+    v = _rand((1, 2, Lk, d), seed + 2)
+    if v_big is not None:
+        v[:, :, jstar] = v_big
+    return tuple(bf16_bits_to_f32(round_to_bf16_bits(a)) for a in (q, k, v))
+
+
+@pytest.mark.parametrize("d", [40, 64, 80])
+@pytest.mark.parametrize("scale", [1.0, 0.5])
+def test_far_key_beyond_first_tile(dev, d, scale):
+    """A key whose score exceeds every score of the first key tile by ~200
+    (scale 1) or ~100 (scale 0.5) binary orders: weights taken relative to an
+    early maximum overflow fp32 in the first case, and must still give the
+    oracle's result."""
+    import torch
+    q, k, v = _aligned_key_case(d, 300 + d)
+    want = oracle.attn(q, k, v, scale)
+    tq, tk, tv = tensors_from_f32(q, k, v, "bf16")
+    for entry in ("auto", "stream"):
+        say(f"far key d={d} scale={scale} {entry}")
+        got = run(entry, tq, tk, tv, scale, torch.float32)
+        assert_bf16_gate(got, want, f"far key d={d} scale={scale} {entry}")
+
+
+@pytest.mark.parametrize("d", [40, 64])
+def test_huge_values_far_key(dev, d):
+    """Weights up to ~2^50 times values of 2^90: the unnormalised output
+    passes fp32's range although every weight and the row sum stay finite.
+    Compared relative to the output's size."""
+    import torch
+    q, k, v = _aligned_key_case(d, 400 + d, v_big=2.0 ** 90)
+    scale = 0.25
+    want = oracle.attn(q, k, v, scale)
+    tq, tk, tv = tensors_from_f32(q, k, v, "bf16")
+    say(f"huge values d={d}")
+    got = run("auto", tq, tk, tv, scale, torch.float32)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    rel = np.abs(got - want).max() / np.abs(want).max()
+    assert rel <= 1e-2, f"relative max error {rel:.3e}"
 
 
 def test_repeatable_bitwise(dev):

@@ -212,25 +212,12 @@ __device__ __forceinline__ void softmax_pv(f32x16 &s, int key0, int Lk, float c,
   }
 }
 
-// Epilogue: divide by the row sum and store this wave's 32 rows.
+// Epilogue: divide by the row sum l and store this wave's 32 rows.
 template <int DK, bool OUT_F32>
-__device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::MT],
-                                          float lsum, void *outp, size_t obase,
-                                          int q0, int Lq, int d, int lane) {
+__device__ __forceinline__ void store_out_l(const f32x16 (&o)[Shape<DK>::MT], float l,
+                                            void *outp, size_t obase, int q0, int Lq,
+                                            int d, int lane) {
   using S = Shape<DK>;
-  float l;
-  if constexpr (S::kOnes) {
-    // Row d of O^T holds sum_j p_j; it sits in the first half-wave.
-    float lv = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < S::MT; ++mt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        if (mt * 32 + 8 * g4 == d) lv = o[mt][4 * g4];
-    l = from_low_half(lv);
-  } else {
-    l = sum_halves(lsum);
-  }
   const float inv = 1.0f / l;
   const int qi = q0 + (lane & 31);
   if (qi >= Lq) return;
@@ -253,6 +240,29 @@ __device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::MT],
         }
       }
     }
+}
+
+// Same, with l taken from the ones row of O^T (padded head dims) or from the
+// per-lane partial sums lsum.
+template <int DK, bool OUT_F32>
+__device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::MT],
+                                          float lsum, void *outp, size_t obase,
+                                          int q0, int Lq, int d, int lane) {
+  using S = Shape<DK>;
+  float l;
+  if constexpr (S::kOnes) {
+    // Row d of O^T holds sum_j p_j; it sits in the first half-wave.
+    float lv = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        if (mt * 32 + 8 * g4 == d) lv = o[mt][4 * g4];
+    l = from_low_half(lv);
+  } else {
+    l = sum_halves(lsum);
+  }
+  store_out_l<DK, OUT_F32>(o, l, outp, obase, q0, Lq, d, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1012,6 +1022,365 @@ void attn_stream_pp_bf16(Bf16Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Streaming kernel, fixed-reference form.
+//
+// Subtracting the row maximum before exponentiating only keeps the weights
+// inside fp32's range: any common reference gives the same normalised result
+// in exact arithmetic, and the weights are rounded to bf16, whose exponent
+// range is fp32's.  This kernel takes the maximum of the first key tile as
+// the reference of the whole row and never rescales, so the loop keeps no
+// running maximum, no per-tile reduction and no data-dependent branch: each
+// iteration is one straight block in which the softmax of tile t (vector
+// ALUs) is interleaved with the scores of tile t+1 and P.V of tile t-1
+// (matrix cores).  Keys far below the reference underflow to zero, which is
+// exact to fp32 precision because the key that set the reference has weight
+// 1.  A key more than ~128 binary orders above it overflows; O or l then ends
+// non-finite, and the wave recomputes its rows with the exact lazily
+// rescaled recurrence, reading K and V straight from memory.
+
+// Exact recurrence for this wave's 32 query rows (32-key sub-tiles, K and V
+// read with buffer loads, no LDS).  Returns the row sum l; O^T in o.
+template <int DK>
+__device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
+                                            const bf16x8 (&qf)[DK / 16], rsrc_t kr,
+                                            rsrc_t vr, int Lk, int d, float c, int lane) {
+  using S = Shape<DK>;
+#pragma unroll
+  for (int mt = 0; mt < S::MT; ++mt) o[mt] = f32x16{};
+  float m_run = -__builtin_inff(), lsum = 0.f;
+  const int h = lane >> 5, r32 = lane & 31;
+  for (int key0 = 0; key0 < Lk; key0 += 32) {
+    f32x16 sv = {};
+#pragma unroll
+    for (int dk = 0; dk < DK / 16; ++dk) {
+      const int c0 = dk * 16 + 8 * h;
+      u32x4 x = bload16(kr, (uint32_t)((key0 + r32) * d + c0) * 2u);
+      if (c0 >= d) x = u32x4{0u, 0u, 0u, 0u};
+      sv = mfma32x32x16(as_bf16x8(x), qf[dk], sv);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (key0 + acc_key(i, lane) >= Lk) sv[i] = -__builtin_inff();
+    float mx = max16(sv, -__builtin_inff());
+    mx = max_halves(mx) * c;  // finite: key0 < Lk is a valid key
+    if (mx > m_run) {
+      const float alpha = fast_exp2(m_run - mx);
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt) o[mt] *= alpha;
+      lsum *= alpha;
+      m_run = mx;
+    }
+    u32x4 pk[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float p8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 8 * kk + j;
+        float x = fast_exp2(__builtin_fmaf(sv[i], c, -m_run));
+        if (key0 + acc_key(i, lane) >= Lk) x = 0.f;
+        lsum += x;
+        p8[j] = x;
+      }
+      pk[kk] = u32x4{pack_bf16x2(p8[0], p8[1]), pack_bf16x2(p8[2], p8[3]),
+                     pack_bf16x2(p8[4], p8[5]), pack_bf16x2(p8[6], p8[7])};
+    }
+    // V^T operand: lane l supplies column 32*mt + l%32 of V at the keys its
+    // weight slots hold (slot j of half h: key 16*kk + 8*(j/4) + 4*h + j%4).
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt) {
+        const int col = 32 * mt + r32;
+        uint32_t w[4];
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) {
+          uint32_t e[2];
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const int j = 2 * j2 + e2;
+            const int key = key0 + 16 * kk + 8 * (j >> 2) + 4 * h + (j & 3);
+            e[e2] = col < d ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                  vr, (uint32_t)(key * d + col) * 2u, 0, 0)
+                            : 0u;
+          }
+          w[j2] = e[0] | (e[1] << 16);
+        }
+        o[mt] = mfma32x32x16(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}),
+                             as_bf16x8(pk[kk]), o[mt]);
+      }
+  }
+  return sum_halves(lsum);
+}
+
+// 16-byte buffer -> LDS transfer issued from inline assembly.  Lane i
+// writes lds + 16*i bytes (lds: byte address in LDS, wave-uniform); source
+// offsets at or past the buffer size write zeros.  The compiler does not see
+// the LDS write, so it adds no wait of its own before later LDS reads (it
+// cannot tell that they touch other buffers, and would otherwise wait for
+// every transfer in flight): the caller orders the transfer with an explicit
+// vmcnt wait and barrier before the data is read, and issues it only into a
+// buffer that every wave has finished reading.  No register receives data.
+__device__ __forceinline__ void dma16_raw(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "m0");
+}
+
+// Raw buffer descriptor words (gfx9 layout: base, stride 0, size in bytes,
+// range-checked raw access).
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, kRsrcWord3};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(lds_void *)const_cast<void *>(p);
+}
+
+template <int DK, bool OUT_F32>
+__global__ __launch_bounds__(4 * kWave, 2)
+void attn_stream_fix_bf16(Bf16Args a) {
+  using S = Shape<DK>;
+  constexpr int NW = 4;
+  using P = DmaPlan<DK, NW>;
+  static_assert(P::BN == 64 && P::NSUB == 2, "64-key tiles");
+  constexpr int BN = P::BN;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[P::NB * (P::KBUF + P::VBUF)];
+  uint16_t *const Ks = smem;
+  uint16_t *const Vs = smem + P::NB * P::KBUF;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = xcd_remap(blockIdx.x, a.nwg);
+  const int bh = wg / a.qblocks;
+  const int q0 = (wg - bh * a.qblocks) * (NW * kQW) + wave * kQW;
+  const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
+  const float c = a.c;
+  const uint16_t *const kbase = a.k + (size_t)bh * Lk * d;
+  const uint16_t *const vbase = a.v + (size_t)bh * Lk * d;
+  const uint32_t kvbytes = (uint32_t)(Lk * d) * 2u;
+  const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
+  const rsrc_t kr = make_rsrc(kbase, kvbytes);
+  const rsrc_t vr = make_rsrc(vbase, kvbytes);
+  const u32x4 kw = rsrc_words(kbase, kvbytes), vw = rsrc_words(vbase, kvbytes);
+  const int n = (Lk + BN - 1) / BN;
+  const bool ragged = (Lk % BN) != 0;
+
+  // Transfers: instruction i = wave + NW*r covers 64 consecutive 16-byte
+  // chunks of a K (i < KI) or V buffer.  K tile u goes to K buffer u % 3 and
+  // V tile u to V buffer u % 3; iteration t starts K tile t+3 and V tile t+1.
+  uint32_t goff[P::NIW];
+  uint32_t loff[P::NIW];  // byte offset within a buffer
+  bool isk[P::NIW], act[P::NIW];
+#pragma unroll
+  for (int r = 0; r < P::NIW; ++r) {
+    const int i = wave + NW * r;
+    isk[r] = i < P::KI;
+    const int blk = isk[r] ? i : i - P::KI;
+    const int cpos = blk * 64 + lane;
+    const int cr = isk[r] ? P::KCR : P::VCR;
+    const int row = cpos / cr, col = cpos - row * cr;
+    act[r] = (i < P::NI) && row < BN && col < d8;
+    goff[r] = (uint32_t)(row * d + col * 8) * 2u;
+    loff[r] = (uint32_t)blk * 1024u;
+  }
+  // Transfers this wave issues per K tile and per V tile (an instruction
+  // with no active lane is branched over and does not count in vmcnt).
+  int kc = 0, vc = 0;
+#pragma unroll
+  for (int r = 0; r < P::NIW; ++r)
+    if (wave + NW * r < P::NI && __any(act[r])) {
+      if (isk[r]) ++kc; else ++vc;
+    }
+  const uint32_t ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
+  auto issue_k = [&](int tt, int b) {
+    const uint32_t toff = (uint32_t)(tt * BN * d) * 2u;
+    const uint32_t dst = ks_lds + (uint32_t)(b * P::KBUF) * 2u;
+#pragma unroll
+    for (int r = 0; r < P::NIW; ++r)
+      if (wave + NW * r < P::NI && isk[r])
+        if (act[r]) dma16_raw(kw, toff + goff[r], dst + loff[r]);
+  };
+  auto issue_v = [&](int tt, int b) {
+    const uint32_t toff = (uint32_t)(tt * BN * d) * 2u;
+    const uint32_t dst = vs_lds + (uint32_t)(b * P::VBUF) * 2u;
+#pragma unroll
+    for (int r = 0; r < P::NIW; ++r)
+      if (wave + NW * r < P::NI && !isk[r])
+        if (act[r]) dma16_raw(vw, toff + goff[r], dst + loff[r]);
+  };
+
+  bf16x8 qf[DK / 16];
+  load_q<DK>(qf, qr, q0, d, a.qsign, lane);
+  issue_k(0, 0);
+  if (n > 1) issue_k(1, 1);
+  if (n > 2) issue_k(2, 2);
+  issue_v(0, 0);
+
+  // Constant columns: K [d, DK) zero; V [d, DV) zero with ones at d.
+  if (d8 < S::DK8) {
+    for (int r = tid; r < P::NB * BN; r += NW * kWave)
+      st16(Ks + r * S::KST + d8 * 8, u32x4{0u, 0u, 0u, 0u});
+  }
+  for (int idx = tid; idx < P::NB * BN * (S::DV / 8); idx += NW * kWave) {
+    const int r = idx / (S::DV / 8), c8 = idx - r * (S::DV / 8);
+    if (c8 >= d8) {
+      const uint32_t w0 = (S::kOnes && c8 == d8) ? uint32_t(kBf16One) : 0u;
+      st16(Vs + r * P::VSTR + c8 * 8, u32x4{w0, 0u, 0u, 0u});
+    }
+  }
+
+  const int koff = (lane & 31) * S::KST + 8 * (lane >> 5);
+  const int g = lane >> 4, pl = lane & 15;
+  const int voff = (4 * (g >> 1) + (pl >> 2)) * P::VSTR + 16 * (g & 1) + 4 * (pl & 3);
+
+  f32x16 o[S::MT];
+#pragma unroll
+  for (int mt = 0; mt < S::MT; ++mt) o[mt] = f32x16{};
+  // Row sums for head dims whose V^T has no padding row to hold ones: an
+  // all-ones A operand makes every row of this accumulator sum the bf16
+  // weights exactly as P.V uses them.
+  f32x16 lacc = {};
+  bf16x8 ones8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones8[i] = (__bf16)1.0f;
+
+  auto scores = [&](int b, f32x16 &s0, f32x16 &s1) {
+    const uint16_t *kb = Ks + b * P::KBUF + koff;
+    s0 = scores_subtile<DK>(kb, qf);
+    s1 = scores_subtile<DK>(kb + 32 * S::KST, qf);
+  };
+  auto pv = [&](int b, const u32x4 (&pk)[4]) {
+    const uint16_t *vb = Vs + b * P::VBUF + voff;
+#pragma unroll
+    for (int kc4 = 0; kc4 < 4; ++kc4)
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt) {
+        const uint16_t *vp = vb + kc4 * 16 * P::VSTR + mt * 32;
+        const s16x4 lo = ld_tr16(vp), hi = ld_tr16(vp + 8 * P::VSTR);
+        const bf16x8 av =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[mt] = mfma32x32x16(av, as_bf16x8(pk[kc4]), o[mt]);
+        if constexpr (!S::kOnes)
+          if (mt == 0) lacc = mfma32x32x16(ones8, as_bf16x8(pk[kc4]), lacc);
+      }
+  };
+
+  // Tile 0's K has landed (K1, K2, V0 may be in flight): scores and the
+  // reference of every row.
+  vmcnt_barrier_rt<2 * P::NIW>((n > 1 ? kc : 0) + (n > 2 ? kc : 0) + vc);
+  f32x16 sA0, sA1, sB0, sB1;
+  scores(0, sA0, sA1);
+  float nm;
+  {
+    f32x16 m0 = sA0, m1 = sA1;
+    if (n == 1 && ragged) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (acc_key(i, lane) >= Lk) m0[i] = -__builtin_inff();
+        if (32 + acc_key(i, lane) >= Lk) m1[i] = -__builtin_inff();
+      }
+    }
+    nm = -(max_halves(max16(m1, max16(m0, -__builtin_inff()))) * c);
+  }
+
+  // Weights of one tile relative to the fixed reference.
+  auto weights = [&](auto mask_c, int key0, const f32x16 &s0, const f32x16 &s1,
+                     u32x4 (&pk)[4]) {
+    constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float p8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * kk + j;
+          float x = fast_exp2(__builtin_fmaf(u == 0 ? s0[i] : s1[i], c, nm));
+          if constexpr (MASK) {
+            if (key0 + 32 * u + acc_key(i, lane) >= Lk) x = 0.f;
+          }
+          p8[j] = x;
+        }
+        pk[2 * u + kk] = u32x4{pack_bf16x2(p8[0], p8[1]), pack_bf16x2(p8[2], p8[3]),
+                               pack_bf16x2(p8[4], p8[5]), pack_bf16x2(p8[6], p8[7])};
+      }
+  };
+
+  // Iteration t: wait for K tile t+1 and V tile t-1 (K t+2 and V t may stay
+  // in flight), start K t+3 and V t+1, then -- one block of independent
+  // work -- scores of tile t+1 (into nx), weights of tile t (from cu, into
+  // pout) and P.V of tile t-1 (weights pin).  Alternate register roles
+  // between consecutive iterations avoid copies.
+  auto body = [&](auto pv_c, auto next_c, auto mask_c, int t, const f32x16 &cu0,
+                  const f32x16 &cu1, f32x16 &nx0, f32x16 &nx1, const u32x4 (&pin)[4],
+                  u32x4 (&pout)[4]) {
+    constexpr bool HAS_PV = decltype(pv_c)::value;
+    constexpr bool HAS_NEXT = decltype(next_c)::value;
+    vmcnt_barrier_rt<P::NIW>((t + 2 < n ? kc : 0) + vc);
+    const int b = t % 3, b1 = b == 2 ? 0 : b + 1, b2 = b == 0 ? 2 : b - 1;
+    if (t + 3 < n) issue_k(t + 3, b);
+    if (t + 1 < n) issue_v(t + 1, b1);
+    if constexpr (HAS_NEXT) scores(b1, nx0, nx1);
+    weights(mask_c, t * BN, cu0, cu1, pout);
+    if constexpr (HAS_PV) pv(b2, pin);
+  };
+  using F = std::integral_constant<bool, false>;
+  using T = std::integral_constant<bool, true>;
+
+  u32x4 pA[4], pB[4];
+  // Last iteration (no next tile) and the P.V of the last tile.
+  auto finish = [&](int t, const f32x16 &cu0, const f32x16 &cu1, const u32x4 (&pin)[4],
+                    u32x4 (&pout)[4]) {
+    if (ragged) body(T{}, F{}, T{}, t, cu0, cu1, sA0, sA1, pin, pout);
+    else body(T{}, F{}, F{}, t, cu0, cu1, sA0, sA1, pin, pout);
+    vmcnt_barrier<0>();
+    pv(t % 3, pout);
+  };
+
+  if (n == 1) {
+    if (ragged) body(F{}, F{}, T{}, 0, sA0, sA1, sB0, sB1, pB, pA);
+    else body(F{}, F{}, F{}, 0, sA0, sA1, sB0, sB1, pB, pA);
+    vmcnt_barrier<0>();
+    pv(0, pA);
+  } else {
+    body(F{}, T{}, F{}, 0, sA0, sA1, sB0, sB1, pB, pA);
+    int t = 1;
+    for (; t + 2 < n; t += 2) {
+      body(T{}, T{}, F{}, t, sB0, sB1, sA0, sA1, pA, pB);
+      body(T{}, T{}, F{}, t + 1, sA0, sA1, sB0, sB1, pB, pA);
+    }
+    if (t + 1 < n) {
+      body(T{}, T{}, F{}, t, sB0, sB1, sA0, sA1, pA, pB);
+      finish(t + 1, sA0, sA1, pB, pA);
+    } else {
+      finish(t, sB0, sB1, pA, pB);
+    }
+  }
+
+  float l;
+  if constexpr (S::kOnes) {
+    float lv = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        if (mt * 32 + 8 * g4 == d) lv = o[mt][4 * g4];
+    l = from_low_half(lv);
+  } else {
+    l = lacc[0];
+  }
+  bool ok = __builtin_isfinite(l);
+#pragma unroll
+  for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ok = ok && __builtin_isfinite(o[mt][i]);
+  if (__any(!ok)) l = rows_exact<DK>(o, qf, kr, vr, Lk, d, c, lane);
+
+  store_out_l<DK, OUT_F32>(o, l, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
+}
+
+// ---------------------------------------------------------------------------
 // Short-key kernel: Lk <= kShortMax, every key resident in LDS.
 
 // Epilogue through LDS: the wave writes its normalised 32 x d tile into a
@@ -1215,7 +1584,15 @@ void attn_short_bf16(Bf16Args a) {
 #ifndef SDATTN_STREAM_PINGPONG
 #define SDATTN_STREAM_PINGPONG 0
 #endif
+#ifndef SDATTN_STREAM_FIX
+#define SDATTN_STREAM_FIX 1
+#endif
+#ifndef SDATTN_STREAM_FIX_MAX_DK
+#define SDATTN_STREAM_FIX_MAX_DK 64
+#endif
 constexpr bool kStreamPingPong = SDATTN_STREAM_PINGPONG != 0;
+constexpr bool kStreamFix = SDATTN_STREAM_FIX != 0;
+constexpr int kStreamFixMaxDk = SDATTN_STREAM_FIX_MAX_DK;
 constexpr int kStreamWaves = SDATTN_STREAM_WAVES;
 constexpr bool kStreamDma = SDATTN_STREAM_DMA != 0;
 constexpr int kShortWaves = SDATTN_SHORT_WAVES;
@@ -1235,6 +1612,18 @@ hipError_t launch_dk(const Bf16Args &base, int BH, bool short_path, bool out_f32
     else
       hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, false>),
                          dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
+  } else if (kStreamFix && DK <= kStreamFixMaxDk) {
+    if constexpr (DK <= kStreamFixMaxDk) {
+      const int per_wg = 4 * kQW;
+      a.qblocks = (a.Lq + per_wg - 1) / per_wg;
+      a.nwg = BH * a.qblocks;
+      if (out_f32)
+        hipLaunchKernelGGL((attn_stream_fix_bf16<DK, true>), dim3(a.nwg), dim3(4 * kWave), 0,
+                           stream, a);
+      else
+        hipLaunchKernelGGL((attn_stream_fix_bf16<DK, false>), dim3(a.nwg), dim3(4 * kWave), 0,
+                           stream, a);
+    }
   } else if (kStreamPingPong && DK <= 160) {
     const int per_wg = 8 * kQW;
     a.qblocks = (a.Lq + per_wg - 1) / per_wg;
