@@ -1122,7 +1122,9 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
 // vmcnt wait and barrier before the data is read, and issues it only into a
 // buffer that every wave has finished reading.  No register receives data.
 __device__ __forceinline__ void dma16_raw(u32x4 rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  // One wait state between the scalar write of M0 and its read by the
+  // transfer (a GFX9-family hazard).
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds), "v"(voff), "s"(rsrc) : "m0");
 }
 
@@ -1137,11 +1139,41 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(lds_void *)const_cast<void *>(p);
 }
 
-template <int DK, bool OUT_F32>
-__global__ __launch_bounds__(4 * kWave, 2)
+// Instruction order for one fixed-reference iteration (a request to the
+// scheduler, mask bits: 0x2 VALU, 0x8 MFMA, 0x100 LDS read): the K reads
+// and half the V reads first, some softmax work while they are in flight,
+// then one matrix instruction followed by VALU_PER vector instructions (and
+// one more V read while any remain), so both units stay busy in one wave.
+#ifndef SDATTN_FIX_SCHED
+#define SDATTN_FIX_SCHED 0
+#endif
+#ifndef SDATTN_FIX_VALU_PER
+#define SDATTN_FIX_VALU_PER 5
+#endif
+template <int I, int NM, int NVR>
+__device__ __forceinline__ void fix_sched_tail() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, SDATTN_FIX_VALU_PER, 0);
+    if constexpr (I < NVR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    fix_sched_tail<I + 1, NM, NVR>();
+  }
+}
+template <int NK, int NV, int NM>
+__device__ __forceinline__ void fix_sched() {
+  if constexpr (SDATTN_FIX_SCHED == 1) {
+    __builtin_amdgcn_sched_group_barrier(0x100, NK + NV / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+    fix_sched_tail<0, NM, NV - NV / 2>();
+  } else if constexpr (SDATTN_FIX_SCHED == 2) {
+    fix_sched_tail<0, NM, 0>();
+  }
+}
+
+template <int DK, int NW, bool OUT_F32>
+__global__ __launch_bounds__(NW * kWave, 8 / NW)
 void attn_stream_fix_bf16(Bf16Args a) {
   using S = Shape<DK>;
-  constexpr int NW = 4;
   using P = DmaPlan<DK, NW>;
   static_assert(P::BN == 64 && P::NSUB == 2, "64-key tiles");
   constexpr int BN = P::BN;
@@ -1285,7 +1317,7 @@ void attn_stream_fix_bf16(Bf16Args a) {
   }
 
   // Weights of one tile relative to the fixed reference.
-  auto weights = [&](auto mask_c, int key0, const f32x16 &s0, const f32x16 &s1,
+  auto weights = [&](auto mask_c, int key0, const f32x16 &s0, const f32x16 &s1, float nmt,
                      u32x4 (&pk)[4]) {
     constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
@@ -1296,7 +1328,7 @@ void attn_stream_fix_bf16(Bf16Args a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * kk + j;
-          float x = fast_exp2(__builtin_fmaf(u == 0 ? s0[i] : s1[i], c, nm));
+          float x = fast_exp2(__builtin_fmaf(u == 0 ? s0[i] : s1[i], c, nmt));
           if constexpr (MASK) {
             if (key0 + 32 * u + acc_key(i, lane) >= Lk) x = 0.f;
           }
@@ -1321,9 +1353,16 @@ void attn_stream_fix_bf16(Bf16Args a) {
     const int b = t % 3, b1 = b == 2 ? 0 : b + 1, b2 = b == 0 ? 2 : b - 1;
     if (t + 3 < n) issue_k(t + 3, b);
     if (t + 1 < n) issue_v(t + 1, b1);
+    // The softmax depends on nothing produced in this iteration; an opaque
+    // copy of the reference keeps the compiler from hoisting it above the
+    // barrier, so it stays in the block it is meant to overlap.
+    float nmt = nm;
+    asm volatile("" : "+v"(nmt));
     if constexpr (HAS_NEXT) scores(b1, nx0, nx1);
-    weights(mask_c, t * BN, cu0, cu1, pout);
+    weights(mask_c, t * BN, cu0, cu1, nmt, pout);
     if constexpr (HAS_PV) pv(b2, pin);
+    if constexpr (HAS_NEXT && HAS_PV)
+      fix_sched<2 * (DK / 16), 8 * S::MT, 2 * (DK / 16) + 4 * S::MT + (S::kOnes ? 0 : 4)>();
   };
   using F = std::integral_constant<bool, false>;
   using T = std::integral_constant<bool, true>;
@@ -1592,7 +1631,11 @@ void attn_short_bf16(Bf16Args a) {
 #endif
 constexpr bool kStreamPingPong = SDATTN_STREAM_PINGPONG != 0;
 constexpr bool kStreamFix = SDATTN_STREAM_FIX != 0;
+#ifndef SDATTN_STREAM_FIX_WAVES
+#define SDATTN_STREAM_FIX_WAVES 8
+#endif
 constexpr int kStreamFixMaxDk = SDATTN_STREAM_FIX_MAX_DK;
+constexpr int kStreamFixWaves = SDATTN_STREAM_FIX_WAVES;
 constexpr int kStreamWaves = SDATTN_STREAM_WAVES;
 constexpr bool kStreamDma = SDATTN_STREAM_DMA != 0;
 constexpr int kShortWaves = SDATTN_SHORT_WAVES;
@@ -1614,15 +1657,16 @@ hipError_t launch_dk(const Bf16Args &base, int BH, bool short_path, bool out_f32
                          dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
   } else if (kStreamFix && DK <= kStreamFixMaxDk) {
     if constexpr (DK <= kStreamFixMaxDk) {
-      const int per_wg = 4 * kQW;
+      constexpr int NW = kStreamFixWaves;
+      const int per_wg = NW * kQW;
       a.qblocks = (a.Lq + per_wg - 1) / per_wg;
       a.nwg = BH * a.qblocks;
       if (out_f32)
-        hipLaunchKernelGGL((attn_stream_fix_bf16<DK, true>), dim3(a.nwg), dim3(4 * kWave), 0,
-                           stream, a);
+        hipLaunchKernelGGL((attn_stream_fix_bf16<DK, NW, true>), dim3(a.nwg), dim3(NW * kWave),
+                           0, stream, a);
       else
-        hipLaunchKernelGGL((attn_stream_fix_bf16<DK, false>), dim3(a.nwg), dim3(4 * kWave), 0,
-                           stream, a);
+        hipLaunchKernelGGL((attn_stream_fix_bf16<DK, NW, false>), dim3(a.nwg), dim3(NW * kWave),
+                           0, stream, a);
     }
   } else if (kStreamPingPong && DK <= 160) {
     const int per_wg = 8 * kQW;
