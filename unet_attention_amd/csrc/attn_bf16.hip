@@ -167,51 +167,6 @@ __device__ __forceinline__ float max16(const f32x16 &s, float m) {
   return m;
 }
 
-// Online-softmax update for one 32-key sub-tile followed by its two P.V
-// chunks.  key0 is the sub-tile's first key; vp points at the sub-tile's
-// first 16-key chunk of V^T for this lane.
-template <int DK, bool MASK>
-__device__ __forceinline__ void softmax_pv(f32x16 &s, int key0, int Lk, float c,
-                                           float &m_run, float &lsum,
-                                           f32x16 (&o)[Shape<DK>::MT],
-                                           const uint16_t *vp, int vst, int lane) {
-  using S = Shape<DK>;
-  if constexpr (MASK) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (key0 + acc_key(i, lane) >= Lk) s[i] = -__builtin_inff();
-  }
-  float mx = max16(s, -__builtin_inff());
-  mx = max_halves(mx);
-  const float mt_new = mx * c;
-  if (__any(mt_new > m_run + kRescaleSlack)) {
-    const float mn = fmaxf(m_run, mt_new);
-    const float alpha = fast_exp2(m_run - mn);
-#pragma unroll
-    for (int mt = 0; mt < S::MT; ++mt) o[mt] *= alpha;
-    lsum *= alpha;
-    m_run = mn;
-  }
-  const float nm = -m_run;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    float p[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = 8 * kk + j;
-      float x = fast_exp2(__builtin_fmaf(s[i], c, nm));
-      if constexpr (MASK) {
-        if (key0 + acc_key(i, lane) >= Lk) x = 0.f;
-      }
-      p[j] = x;
-      if constexpr (!S::kOnes) lsum += x;
-    }
-    const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-    pv_chunk<DK>(o, vp + kk * 16, vst, as_bf16x8(pk));
-  }
-}
-
 // Epilogue: divide by the row sum l and store this wave's 32 rows.
 template <int DK, bool OUT_F32>
 __device__ __forceinline__ void store_out_l(const f32x16 (&o)[Shape<DK>::MT], float l,
@@ -266,251 +221,6 @@ __device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::MT],
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel: any Lk >= 1.
-
-// Streaming schedule: software-pipelined (scores of tile t+1 issued before
-// the softmax of tile t, three K buffers) or plain double buffering.
-#ifndef SDATTN_STREAM_PIPELINED
-#define SDATTN_STREAM_PIPELINED 0
-#endif
-constexpr bool kPipelined = SDATTN_STREAM_PIPELINED != 0;
-
-// Keys per streamed tile: 64, or 32 for the widest head dims so that three
-// K buffers and two V^T buffers stay within the 160 KB of LDS.
-template <int DK>
-constexpr int stream_bn() { return DK <= 224 ? 64 : 32; }
-
-template <int DK, int NW>
-struct StreamPlan {
-  using S = Shape<DK>;
-  static constexpr int BN = stream_bn<DK>();
-  static constexpr int NSUB = BN / 32;                       // 32-key sub-tiles
-  static constexpr int NT = NW * kWave;
-  static constexpr int VST = BN + 8;                         // V^T row stride
-  static constexpr int KCH = (BN * S::DK8 + NT - 1) / NT;    // K chunks / thread
-  static constexpr int VG = BN / 4;                          // 4-key groups
-  static constexpr int VCH = (VG * S::DK8 + NT - 1) / NT;    // V units / thread
-  static constexpr int KBUF = BN * S::KST;                   // elements per K buffer
-  static constexpr int VBUF = S::DV * VST;                   // elements per V^T buffer
-};
-
-// Per-thread staging state: which K chunks and V units this thread moves
-// from HBM/L2 into LDS.  K chunks are handed out from the first wave, V
-// units from the last, so the two jobs land on different waves.
-template <int DK, int NW>
-struct Stager {
-  using P = StreamPlan<DK, NW>;
-  uint32_t k_goff[P::KCH];   // byte offset within a tile (global)
-  int k_loff[P::KCH];        // element offset in an LDS K buffer, -1 = idle
-  uint32_t v_goff[P::VCH];   // byte offset of the unit's first row within a tile
-  int v_row0[P::VCH];        // first V^T row (column of V), -1 = idle
-  int v_g[P::VCH];           // 4-key group
-  u32x4 kreg[P::KCH];
-  u32x4 vreg[P::VCH][4];
-
-  __device__ __forceinline__ void init(int tid, int d) {
-    const int d8 = d >> 3;
-#pragma unroll
-    for (int t = 0; t < P::KCH; ++t) {
-      const int idx = tid + t * P::NT;
-      const int row = idx / d8, ch = idx - row * d8;
-      const bool ok = idx < P::BN * d8;
-      k_goff[t] = (uint32_t)idx * 16u;
-      k_loff[t] = ok ? row * Shape<DK>::KST + ch * 8 : -1;
-    }
-#pragma unroll
-    for (int t = 0; t < P::VCH; ++t) {
-      const int u = (P::NT - 1 - tid) + t * P::NT;
-      const int g = u % P::VG, ch = u / P::VG;
-      const bool ok = u < P::VG * d8;
-      v_goff[t] = (uint32_t)(4 * g * d + ch * 8) * 2u;
-      v_row0[t] = ok ? ch * 8 : -1;
-      v_g[t] = g;
-    }
-  }
-
-  // Issue the loads of the K / V tile starting at key j0 (rows >= Lk read
-  // zero through the buffer range check).
-  __device__ __forceinline__ void load_k(rsrc_t kr, int j0, int d) {
-    const uint32_t base = (uint32_t)(j0 * d) * 2u;
-#pragma unroll
-    for (int t = 0; t < P::KCH; ++t)
-      if (k_loff[t] >= 0) kreg[t] = bload16(kr, base + k_goff[t]);
-  }
-  __device__ __forceinline__ void load_v(rsrc_t vr, int j0, int d) {
-    const uint32_t base = (uint32_t)(j0 * d) * 2u, row = (uint32_t)d * 2u;
-#pragma unroll
-    for (int t = 0; t < P::VCH; ++t)
-      if (v_row0[t] >= 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vreg[t][r] = bload16(vr, base + v_goff[t] + r * row);
-      }
-  }
-  __device__ __forceinline__ void store_k(uint16_t *ks) {
-#pragma unroll
-    for (int t = 0; t < P::KCH; ++t)
-      if (k_loff[t] >= 0) st16(ks + k_loff[t], kreg[t]);
-  }
-  __device__ __forceinline__ void store_v(uint16_t *vt) {
-#pragma unroll
-    for (int t = 0; t < P::VCH; ++t)
-      if (v_row0[t] >= 0) store_vt_unit(vt, P::VST, v_row0[t], v_g[t], vreg[t]);
-  }
-};
-
-// Software pipeline, per iteration t (one tile of BN keys):
-//   issue the HBM/L2 loads of K[t+2] and V[t+1] into registers;
-//   S[t+1] = K[t+1] Q^T on the matrix cores (asynchronous) while the vector
-//   ALUs run the softmax of S[t] (computed in the previous iteration);
-//   O^T += V[t]^T P[t]^T;
-//   write K[t+2], V[t+1] to LDS; one barrier.
-// K cycles through three LDS buffers (t+1 is read while t+2 is written and
-// t's buffer may still be read by a slower wave), V^T through two.
-template <int DK, int NW, bool OUT_F32>
-__global__ __launch_bounds__(NW * kWave, (min_blocks<DK, NW>()))
-void attn_stream_bf16(Bf16Args a) {
-  using S = Shape<DK>;
-  using P = StreamPlan<DK, NW>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[(kPipelined ? 3 : 2) * P::KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * P::VBUF];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wg = xcd_remap(blockIdx.x, a.nwg);
-  const int bh = wg / a.qblocks;
-  const int q0 = (wg - bh * a.qblocks) * (NW * kQW) + wave * kQW;
-  const int d = a.d, Lk = a.Lk, Lq = a.Lq;
-  const float c = a.c;
-  const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
-  const rsrc_t kr = make_rsrc(a.k + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
-  const rsrc_t vr = make_rsrc(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
-  constexpr int BN = P::BN, NSUB = P::NSUB;
-  const int ntiles = (Lk + BN - 1) / BN;
-  const bool ragged = (Lk % BN) != 0;
-
-  Stager<DK, NW> st;
-  st.init(tid, d);
-  st.load_k(kr, 0, d);
-  st.load_v(vr, 0, d);
-
-  bf16x8 qf[DK / 16];
-  load_q<DK>(qf, qr, q0, d, a.qsign, lane);
-
-  init_k_pad<DK, (kPipelined ? 3 : 2) * BN>(Ks, d, tid, P::NT);
-  init_vt_const<DK, BN>(Vt, P::VST, d, tid, P::NT);
-  init_vt_const<DK, BN>(Vt + P::VBUF, P::VST, d, tid, P::NT);
-
-  st.store_k(Ks);
-  st.store_v(Vt);
-  if (kPipelined && ntiles > 1) {
-    st.load_k(kr, BN, d);
-    st.store_k(Ks + P::KBUF);
-  }
-  __syncthreads();
-
-  // Per-lane LDS read bases: K rows (l % 32), V^T rows (l % 32).
-  const int koff = (lane & 31) * S::KST + 8 * (lane >> 5);
-  const int voff = (lane & 31) * P::VST + 8 * (lane >> 5);
-
-  f32x16 o[S::MT];
-#pragma unroll
-  for (int mt = 0; mt < S::MT; ++mt) o[mt] = f32x16{};
-  float m_run = -__builtin_inff();  // running max, log2 domain
-  float lsum = 0.f;                 // partial row sum (when not from MFMA)
-
-  using Full = std::integral_constant<bool, false>;
-  using Ragged = std::integral_constant<bool, true>;
-
-  // Softmax and P.V of one tile whose scores are in (c0, c1); MASK marks the
-  // ragged last tile.
-  auto softmax_tile = [&](auto mask_c, f32x16 &c0, f32x16 &c1, int j0,
-                          const uint16_t *vb) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    softmax_pv<DK, MASK>(c0, j0, Lk, c, m_run, lsum, o, vb, P::VST, lane);
-    if constexpr (NSUB == 2)
-      softmax_pv<DK, MASK>(c1, j0 + 32, Lk, c, m_run, lsum, o, vb + 32, P::VST, lane);
-  };
-  auto scores_tile = [&](const uint16_t *kb, f32x16 &c0, f32x16 &c1) {
-    c0 = scores_subtile<DK>(kb, qf);
-    if constexpr (NSUB == 2) c1 = scores_subtile<DK>(kb + 32 * S::KST, qf);
-  };
-
-  if constexpr (kPipelined) {
-    // Two register sets alternate between the current tile's scores and the
-    // next tile's (the loop is unrolled by two), so nothing is copied.
-    f32x16 sa0, sa1, sb0, sb1;
-    scores_tile(Ks + koff, sa0, sa1);
-    int kb_next = 1;  // LDS K buffer holding tile t+1
-    // Iteration t < ntiles-1: a next tile exists.
-    auto iter = [&](f32x16 &c0, f32x16 &c1, f32x16 &n0, f32x16 &n1, int t) {
-      const int j0 = t * BN;
-      const bool has_next2 = t + 2 < ntiles;
-      if (has_next2) st.load_k(kr, j0 + 2 * BN, d);
-      st.load_v(vr, j0 + BN, d);
-      scores_tile(Ks + kb_next * P::KBUF + koff, n0, n1);
-      softmax_tile(Full{}, c0, c1, j0, Vt + (t & 1) * P::VBUF + voff);
-      const int kb_next2 = (kb_next == 2) ? 0 : kb_next + 1;
-      if (has_next2) st.store_k(Ks + kb_next2 * P::KBUF);
-      st.store_v(Vt + ((t + 1) & 1) * P::VBUF);
-      __syncthreads();
-      kb_next = kb_next2;
-    };
-    auto last = [&](f32x16 &c0, f32x16 &c1, int t) {
-      const uint16_t *vb = Vt + (t & 1) * P::VBUF + voff;
-      if (ragged) softmax_tile(Ragged{}, c0, c1, t * BN, vb);
-      else softmax_tile(Full{}, c0, c1, t * BN, vb);
-    };
-    int t = 0;
-    for (; t + 2 < ntiles; t += 2) {
-      iter(sa0, sa1, sb0, sb1, t);
-      iter(sb0, sb1, sa0, sa1, t + 1);
-    }
-    if (t + 1 < ntiles) {
-      iter(sa0, sa1, sb0, sb1, t);
-      last(sb0, sb1, t + 1);
-    } else {
-      last(sa0, sa1, t);
-    }
-  } else {
-    // Double buffering: tile t+1 is staged while tile t is computed; the
-    // loop is unrolled by two so both buffers have fixed LDS addresses.
-    const int nfull = Lk / BN;
-    auto step = [&](auto buf_c, auto mask_c, int t) {
-      constexpr int BUF = decltype(buf_c)::value;
-      const int j0 = t * BN;
-      const bool more = t + 1 < ntiles;
-      if (more) {
-        st.load_k(kr, j0 + BN, d);
-        st.load_v(vr, j0 + BN, d);
-      }
-      f32x16 c0, c1;
-      scores_tile(Ks + BUF * P::KBUF + koff, c0, c1);
-      softmax_tile(mask_c, c0, c1, j0, Vt + BUF * P::VBUF + voff);
-      if (more) {
-        st.store_k(Ks + (1 - BUF) * P::KBUF);
-        st.store_v(Vt + (1 - BUF) * P::VBUF);
-      }
-      __syncthreads();
-    };
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    int t = 0;
-    for (; t + 2 <= nfull; t += 2) {
-      step(B0{}, Full{}, t);
-      step(B1{}, Full{}, t + 1);
-    }
-    if (t < nfull) {
-      step(B0{}, Full{}, t);
-      ++t;
-      if (t < ntiles) step(B1{}, Ragged{}, t);
-    } else if (t < ntiles) {
-      step(B0{}, Ragged{}, t);
-    }
-  }
-
-  store_out<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
-}
-
-// ---------------------------------------------------------------------------
 // Streaming kernel, DMA form (default): K and V tiles go from HBM straight
 // into LDS with buffer->LDS transfers, so no registers, LDS writes or vector
 // instructions are spent on staging, and three LDS buffers let the transfer
@@ -533,12 +243,38 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// 16-byte buffer -> LDS transfer for every active lane: lane i writes
-// lds + 16*i bytes (lds is wave-uniform); offsets at or past the buffer size
-// write zeros.
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint16_t *lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, 0, 0, 0);
+// 16-byte buffer -> LDS transfer issued from inline assembly.  Lane i
+// writes lds + 16*i bytes (lds: byte address in LDS, wave-uniform); source
+// offsets at or past the buffer size write zeros.  The compiler does not see
+// the LDS write, so it adds no wait of its own before later LDS reads (it
+// cannot tell that they touch other buffers, and would otherwise wait for
+// every transfer in flight): the caller orders the transfer with an explicit
+// vmcnt wait and barrier before the data is read, and issues it only into a
+// buffer that every wave has finished reading.  No register receives data.
+// M0 is declared clobbered; nothing the compiler generates for these kernels
+// keeps a value in M0 (no compiler-issued LDS transfers, GWS or indexed
+// register moves), so the clobber warning does not apply.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_raw(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  // One wait state between the scalar write of M0 and its read by the
+  // transfer (a GFX9-family hazard).
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "m0");
 }
+#pragma clang diagnostic pop
+
+// Raw buffer descriptor words (gfx9 layout: base, stride 0, size in bytes,
+// range-checked raw access).
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, kRsrcWord3};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(lds_void *)const_cast<void *>(p);
+}
+
 
 __device__ __forceinline__ s16x4 ld_tr16(const uint16_t *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)const_cast<uint16_t *>(p));
@@ -616,8 +352,8 @@ void attn_stream_dma_bf16(Bf16Args a) {
   const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
   const float c = a.c;
   const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
-  const rsrc_t kr = make_rsrc(a.k + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
-  const rsrc_t vr = make_rsrc(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  const u32x4 kw = rsrc_words(a.k + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  const u32x4 vw = rsrc_words(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
   const int ntiles = (Lk + BN - 1) / BN;
   const bool ragged = (Lk % BN) != 0;
 
@@ -650,9 +386,9 @@ void attn_stream_dma_bf16(Bf16Args a) {
     for (int r = 0; r < P::NIW; ++r) {
       if (wave + NW * r < P::NI) {
         if (isk[r]) {
-          if (act[r]) dma16(kr, toff + goff[r], Ks + b * P::KBUF + loff[r]);
+          if (act[r]) dma16_raw(kw, toff + goff[r], lds_addr(Ks + b * P::KBUF + loff[r]));
         } else {
-          if (act[r]) dma16(vr, toff + goff[r], Vs + b * P::VBUF + loff[r]);
+          if (act[r]) dma16_raw(vw, toff + goff[r], lds_addr(Vs + b * P::VBUF + loff[r]));
         }
       }
     }
@@ -788,240 +524,6 @@ void attn_stream_dma_bf16(Bf16Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel, ping-pong form.  A workgroup is eight waves (two per
-// SIMD, 256 query rows).  Each wave alternates two phases per key tile:
-//   M_t: S_t = K_t Q^T and O^T += V_{t-1}^T P_{t-1}^T  (matrix cores)
-//   V_t: online softmax of S_t -> P_t (bf16)           (vector ALUs)
-// Waves 0-3 ("A") run phase h in half-period h, waves 4-7 ("B") run phase
-// h-1, with a workgroup barrier between half-periods, so on every SIMD one
-// wave issues matrix instructions while the other does the softmax: on
-// MI355X a VALU-only wave overlaps an MFMA-only wave on the same SIMD far
-// better than the two instruction kinds overlap within one wave.  K/V tiles
-// arrive by buffer->LDS transfers two tiles ahead in four LDS buffers; the
-// ragged last tile (if any) is computed after the loop by all waves at once.
-
-template <int DK>
-constexpr int pp_bn() {
-  // 64-key tiles need two score accumulators per wave: above 128 columns
-  // they no longer fit the 256 VGPRs beside the O accumulators.
-  return DK <= 128 && 4 * 64 * (Shape<DK>::KST + dma_vstr<DK>()) * 2 <= 160 * 1024 ? 64 : 32;
-}
-
-template <int DK>
-struct PPPlan {
-  using S = Shape<DK>;
-  static constexpr int NW = 8;
-  static constexpr int BN = pp_bn<DK>();
-  static constexpr int NSUB = BN / 32;
-  static constexpr int NB = 4;
-  static constexpr int KCR = S::KST / 8;
-  static constexpr int VSTR = dma_vstr<DK>();
-  static constexpr int VCR = VSTR / 8;
-  static constexpr int KBUF = BN * S::KST;
-  static constexpr int VBUF = BN * VSTR;
-  static constexpr int KI = (BN * KCR + 63) / 64;
-  static constexpr int VI = (BN * VCR + 63) / 64;
-  static constexpr int NI = KI + VI;
-  static constexpr int NIW = (NI + NW - 1) / NW;
-};
-
-template <int DK, bool OUT_F32>
-__global__ __launch_bounds__(8 * kWave, 1)
-void attn_stream_pp_bf16(Bf16Args a) {
-  using S = Shape<DK>;
-  using P = PPPlan<DK>;
-  constexpr int NW = P::NW, BN = P::BN, NSUB = P::NSUB;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[P::NB * (P::KBUF + P::VBUF)];
-  uint16_t *const Ks = smem;
-  uint16_t *const Vs = smem + P::NB * P::KBUF;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;  // 0: leads by half a period, 1: lags
-  const int wg = xcd_remap(blockIdx.x, a.nwg);
-  const int bh = wg / a.qblocks;
-  const int q0 = (wg - bh * a.qblocks) * (NW * kQW) + wave * kQW;
-  const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
-  const float c = a.c;
-  const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
-  const rsrc_t kr = make_rsrc(a.k + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
-  const rsrc_t vr = make_rsrc(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
-  const int ntiles = (Lk + BN - 1) / BN;
-  const int nfull = Lk / BN;
-
-  // Transfers: instruction i = wave + NW*r covers 64 consecutive 16-byte
-  // chunks of a K (i < KI) or V buffer.
-  uint32_t goff[P::NIW];
-  int loff[P::NIW];
-  bool isk[P::NIW], act[P::NIW];
-#pragma unroll
-  for (int r = 0; r < P::NIW; ++r) {
-    const int i = wave + NW * r;
-    isk[r] = i < P::KI;
-    const int blk = isk[r] ? i : i - P::KI;
-    const int cpos = blk * 64 + lane;
-    const int cr = isk[r] ? P::KCR : P::VCR;
-    const int row = cpos / cr, col = cpos - row * cr;
-    act[r] = (i < P::NI) && row < BN && col < d8;
-    goff[r] = (uint32_t)(row * d + col * 8) * 2u;
-    loff[r] = blk * 512;
-  }
-  int my_count = 0;
-#pragma unroll
-  for (int r = 0; r < P::NIW; ++r)
-    if (wave + NW * r < P::NI && __any(act[r])) ++my_count;
-  auto issue = [&](int tt) {
-    const int b = tt & 3;
-    const uint32_t toff = (uint32_t)(tt * BN * d) * 2u;
-#pragma unroll
-    for (int r = 0; r < P::NIW; ++r) {
-      if (wave + NW * r < P::NI) {
-        if (isk[r]) {
-          if (act[r]) dma16(kr, toff + goff[r], Ks + b * P::KBUF + loff[r]);
-        } else {
-          if (act[r]) dma16(vr, toff + goff[r], Vs + b * P::VBUF + loff[r]);
-        }
-      }
-    }
-  };
-
-  bf16x8 qf[DK / 16];
-  load_q<DK>(qf, qr, q0, d, a.qsign, lane);
-  issue(0);
-  if (ntiles > 1) issue(1);
-  if (d8 < S::DK8) {
-    for (int r = tid; r < P::NB * BN; r += NW * kWave)
-      st16(Ks + r * S::KST + d8 * 8, u32x4{0u, 0u, 0u, 0u});
-  }
-  for (int idx = tid; idx < P::NB * BN * (S::DV / 8); idx += NW * kWave) {
-    const int r = idx / (S::DV / 8), c8 = idx - r * (S::DV / 8);
-    if (c8 >= d8) {
-      const uint32_t w0 = (S::kOnes && c8 == d8) ? uint32_t(kBf16One) : 0u;
-      st16(Vs + r * P::VSTR + c8 * 8, u32x4{w0, 0u, 0u, 0u});
-    }
-  }
-
-  const int koff = (lane & 31) * S::KST + 8 * (lane >> 5);
-  const int gq = lane >> 4, pl = lane & 15;
-  const int voff = (4 * (gq >> 1) + (pl >> 2)) * P::VSTR + 16 * (gq & 1) + 4 * (pl & 3);
-
-  f32x16 o[S::MT];
-#pragma unroll
-  for (int mt = 0; mt < S::MT; ++mt) o[mt] = f32x16{};
-  float m_run = -__builtin_inff();
-  float lsum = 0.f;
-  f32x16 s0, s1;        // scores of the tile whose softmax comes next
-  u32x4 pk[2 * NSUB];   // bf16 weights of the tile whose P.V comes next
-
-  auto scores = [&](int t) {
-    const uint16_t *kb = Ks + (t & 3) * P::KBUF + koff;
-    s0 = scores_subtile<DK>(kb, qf);
-    if constexpr (NSUB == 2) s1 = scores_subtile<DK>(kb + 32 * S::KST, qf);
-  };
-  auto pv = [&](int t) {
-    const uint16_t *vb = Vs + (t & 3) * P::VBUF + voff;
-#pragma unroll
-    for (int kc = 0; kc < 2 * NSUB; ++kc) {
-#pragma unroll
-      for (int mt = 0; mt < S::MT; ++mt) {
-        const uint16_t *vp = vb + kc * 16 * P::VSTR + mt * 32;
-        const s16x4 lo = ld_tr16(vp), hi = ld_tr16(vp + 8 * P::VSTR);
-        const bf16x8 av =
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mt] = mfma32x32x16(av, as_bf16x8(pk[kc]), o[mt]);
-      }
-    }
-  };
-  // Softmax of one key tile into weights pk[0 .. 2*NSUB-1].  One maximum
-  // over the whole tile decides the rescale before any weight is formed:
-  // P.V of this tile runs in a later phase, so weights formed under a
-  // maximum that is raised afterwards would never be corrected.
-  auto soft_tile = [&](auto mask_c, int key0) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    if constexpr (MASK) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (key0 + acc_key(i, lane) >= Lk) s0[i] = -__builtin_inff();
-        if constexpr (NSUB == 2)
-          if (key0 + 32 + acc_key(i, lane) >= Lk) s1[i] = -__builtin_inff();
-      }
-    }
-    float mx = max16(s0, -__builtin_inff());
-    if constexpr (NSUB == 2) mx = max16(s1, mx);
-    mx = max_halves(mx);
-    const float mt_new = mx * c;
-    if (__any(mt_new > m_run + kRescaleSlack)) {
-      const float mn = fmaxf(m_run, mt_new);
-      const float alpha = fast_exp2(m_run - mn);
-#pragma unroll
-      for (int mt = 0; mt < S::MT; ++mt) o[mt] *= alpha;
-      lsum *= alpha;
-      m_run = mn;
-    }
-    const float nm = -m_run;
-#pragma unroll
-    for (int u = 0; u < NSUB; ++u) {
-      const f32x16 &sv = u == 0 ? s0 : s1;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        float pv8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * kk + j;
-          float x = fast_exp2(__builtin_fmaf(sv[i], c, nm));
-          if constexpr (MASK) {
-            if (key0 + 32 * u + acc_key(i, lane) >= Lk) x = 0.f;
-          }
-          pv8[j] = x;
-          if constexpr (!S::kOnes) lsum += x;
-        }
-        pk[2 * u + kk] = u32x4{pack_bf16x2(pv8[0], pv8[1]), pack_bf16x2(pv8[2], pv8[3]),
-                               pack_bf16x2(pv8[4], pv8[5]), pack_bf16x2(pv8[6], pv8[7])};
-      }
-    }
-  };
-  using Full = std::integral_constant<bool, false>;
-  using Ragged = std::integral_constant<bool, true>;
-
-  // Tile 0 must have landed; tile 1 may still be in flight.
-  vmcnt_barrier_rt<P::NIW>(ntiles > 1 ? my_count : 0);
-
-  const int n = nfull;
-  for (int h = 0; h < 2 * n + 2; ++h) {
-    if ((h & 1) == 0 && (h >> 1) + 2 < ntiles) issue((h >> 1) + 2);
-    const int ph = h - grp;
-    if (ph >= 0) {
-      const int t = ph >> 1;
-      if ((ph & 1) == 0) {
-        __builtin_amdgcn_s_setprio(1);
-        if (t < n) scores(t);
-        if (t >= 1 && t <= n) pv(t - 1);
-        __builtin_amdgcn_s_setprio(0);
-      } else if (t < n) {
-        soft_tile(Full{}, t * BN);
-      }
-    }
-    // Entering half-period h+1; if it starts tile (h+1)/2's matrix phase,
-    // that tile must have landed (the next one may still be in flight).
-    const int tn = (h + 1) >> 1;
-    if (((h + 1) & 1) == 0 && tn < ntiles)
-      vmcnt_barrier_rt<P::NIW>(tn + 1 < ntiles ? my_count : 0);
-    else
-      vmcnt_barrier<0>();
-  }
-
-  if (nfull < ntiles) {
-    // Ragged last tile, all waves together (its transfer has landed: the
-    // loop's barrier entering half-period 2*nfull waited for it).
-    scores(nfull);
-    soft_tile(Ragged{}, nfull * BN);
-    pv(nfull);
-  }
-
-  store_out<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
-}
-
-// ---------------------------------------------------------------------------
 // Streaming kernel, fixed-reference form.
 //
 // Subtracting the row maximum before exponentiating only keeps the weights
@@ -1113,62 +615,12 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
   return sum_halves(lsum);
 }
 
-// 16-byte buffer -> LDS transfer issued from inline assembly.  Lane i
-// writes lds + 16*i bytes (lds: byte address in LDS, wave-uniform); source
-// offsets at or past the buffer size write zeros.  The compiler does not see
-// the LDS write, so it adds no wait of its own before later LDS reads (it
-// cannot tell that they touch other buffers, and would otherwise wait for
-// every transfer in flight): the caller orders the transfer with an explicit
-// vmcnt wait and barrier before the data is read, and issues it only into a
-// buffer that every wave has finished reading.  No register receives data.
-__device__ __forceinline__ void dma16_raw(u32x4 rsrc, uint32_t voff, uint32_t lds) {
-  // One wait state between the scalar write of M0 and its read by the
-  // transfer (a GFX9-family hazard).
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc) : "m0");
-}
-
-// Raw buffer descriptor words (gfx9 layout: base, stride 0, size in bytes,
-// range-checked raw access).
-__device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, kRsrcWord3};
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)(lds_void *)const_cast<void *>(p);
-}
-
-// Instruction order for one fixed-reference iteration (a request to the
-// scheduler, mask bits: 0x2 VALU, 0x8 MFMA, 0x100 LDS read): the K reads
-// and half the V reads first, some softmax work while they are in flight,
-// then one matrix instruction followed by VALU_PER vector instructions (and
-// one more V read while any remain), so both units stay busy in one wave.
-#ifndef SDATTN_FIX_SCHED
-#define SDATTN_FIX_SCHED 0
+// LDS buffers per operand in the fixed-reference kernel: K tiles are
+// requested NB iterations ahead, V tiles NB-2 ahead (3 measured best).
+#ifndef SDATTN_FIX_BUFFERS
+#define SDATTN_FIX_BUFFERS 3
 #endif
-#ifndef SDATTN_FIX_VALU_PER
-#define SDATTN_FIX_VALU_PER 5
-#endif
-template <int I, int NM, int NVR>
-__device__ __forceinline__ void fix_sched_tail() {
-  if constexpr (I < NM) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, SDATTN_FIX_VALU_PER, 0);
-    if constexpr (I < NVR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    fix_sched_tail<I + 1, NM, NVR>();
-  }
-}
-template <int NK, int NV, int NM>
-__device__ __forceinline__ void fix_sched() {
-  if constexpr (SDATTN_FIX_SCHED == 1) {
-    __builtin_amdgcn_sched_group_barrier(0x100, NK + NV / 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-    fix_sched_tail<0, NM, NV - NV / 2>();
-  } else if constexpr (SDATTN_FIX_SCHED == 2) {
-    fix_sched_tail<0, NM, 0>();
-  }
-}
+constexpr int kFixBuffers = SDATTN_FIX_BUFFERS;
 
 template <int DK, int NW, bool OUT_F32>
 __global__ __launch_bounds__(NW * kWave, 8 / NW)
@@ -1177,9 +629,11 @@ void attn_stream_fix_bf16(Bf16Args a) {
   using P = DmaPlan<DK, NW>;
   static_assert(P::BN == 64 && P::NSUB == 2, "64-key tiles");
   constexpr int BN = P::BN;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[P::NB * (P::KBUF + P::VBUF)];
+  constexpr int NB = kFixBuffers;  // LDS buffers per operand
+  static_assert(NB >= 3, "K runs NB tiles ahead, V NB-2 tiles ahead");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NB * (P::KBUF + P::VBUF)];
   uint16_t *const Ks = smem;
-  uint16_t *const Vs = smem + P::NB * P::KBUF;
+  uint16_t *const Vs = smem + NB * P::KBUF;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1199,8 +653,9 @@ void attn_stream_fix_bf16(Bf16Args a) {
   const bool ragged = (Lk % BN) != 0;
 
   // Transfers: instruction i = wave + NW*r covers 64 consecutive 16-byte
-  // chunks of a K (i < KI) or V buffer.  K tile u goes to K buffer u % 3 and
-  // V tile u to V buffer u % 3; iteration t starts K tile t+3 and V tile t+1.
+  // chunks of a K (i < KI) or V buffer.  K tile u goes to K buffer u % NB and
+  // V tile u to V buffer u % NB; iteration j starts K tile j+NB and V tile
+  // j+NB-2 (the prologue plays iterations -NB .. -1).
   uint32_t goff[P::NIW];
   uint32_t loff[P::NIW];  // byte offset within a buffer
   bool isk[P::NIW], act[P::NIW];
@@ -1242,19 +697,26 @@ void attn_stream_fix_bf16(Bf16Args a) {
         if (act[r]) dma16_raw(vw, toff + goff[r], dst + loff[r]);
   };
 
+  // Transfers this wave issues in iteration j (prologue included).
+  auto issued = [&](int j) {
+    const int vk = j + NB - 2;
+    return (j + NB < n ? kc : 0) + (vk >= 0 && vk < n ? vc : 0);
+  };
+
   bf16x8 qf[DK / 16];
   load_q<DK>(qf, qr, q0, d, a.qsign, lane);
-  issue_k(0, 0);
-  if (n > 1) issue_k(1, 1);
-  if (n > 2) issue_k(2, 2);
-  issue_v(0, 0);
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    if (u < n) issue_k(u, u);
+    if (u >= 2 && u - 2 < n) issue_v(u - 2, u - 2);
+  }
 
   // Constant columns: K [d, DK) zero; V [d, DV) zero with ones at d.
   if (d8 < S::DK8) {
-    for (int r = tid; r < P::NB * BN; r += NW * kWave)
+    for (int r = tid; r < NB * BN; r += NW * kWave)
       st16(Ks + r * S::KST + d8 * 8, u32x4{0u, 0u, 0u, 0u});
   }
-  for (int idx = tid; idx < P::NB * BN * (S::DV / 8); idx += NW * kWave) {
+  for (int idx = tid; idx < NB * BN * (S::DV / 8); idx += NW * kWave) {
     const int r = idx / (S::DV / 8), c8 = idx - r * (S::DV / 8);
     if (c8 >= d8) {
       const uint32_t w0 = (S::kOnes && c8 == d8) ? uint32_t(kBf16One) : 0u;
@@ -1298,9 +760,14 @@ void attn_stream_fix_bf16(Bf16Args a) {
       }
   };
 
-  // Tile 0's K has landed (K1, K2, V0 may be in flight): scores and the
-  // reference of every row.
-  vmcnt_barrier_rt<2 * P::NIW>((n > 1 ? kc : 0) + (n > 2 ? kc : 0) + vc);
+  // Tile 0's K has landed (everything the prologue issued after it may be
+  // in flight): scores and the reference of every row.
+  {
+    int after = issued(-NB) - kc;
+#pragma unroll
+    for (int j = 1 - NB; j < 0; ++j) after += issued(j);
+    vmcnt_barrier_rt<NB * P::NIW>(after);
+  }
   f32x16 sA0, sA1, sB0, sB1;
   scores(0, sA0, sA1);
   float nm;
@@ -1339,8 +806,9 @@ void attn_stream_fix_bf16(Bf16Args a) {
       }
   };
 
-  // Iteration t: wait for K tile t+1 and V tile t-1 (K t+2 and V t may stay
-  // in flight), start K t+3 and V t+1, then -- one block of independent
+  // Iteration t: wait for K tile t+1 and V tile t-1 (both started in
+  // iteration t+1-NB; later ones may stay in flight), start K t+NB and
+  // V t+NB-2 into the buffers read in iteration t-1, then -- one block of independent
   // work -- scores of tile t+1 (into nx), weights of tile t (from cu, into
   // pout) and P.V of tile t-1 (weights pin).  Alternate register roles
   // between consecutive iterations avoid copies.
@@ -1349,10 +817,16 @@ void attn_stream_fix_bf16(Bf16Args a) {
                   u32x4 (&pout)[4]) {
     constexpr bool HAS_PV = decltype(pv_c)::value;
     constexpr bool HAS_NEXT = decltype(next_c)::value;
-    vmcnt_barrier_rt<P::NIW>((t + 2 < n ? kc : 0) + vc);
-    const int b = t % 3, b1 = b == 2 ? 0 : b + 1, b2 = b == 0 ? 2 : b - 1;
-    if (t + 3 < n) issue_k(t + 3, b);
-    if (t + 1 < n) issue_v(t + 1, b1);
+    {
+      int later = 0;
+#pragma unroll
+      for (int j = t + 2 - NB; j < t; ++j) later += issued(j);
+      vmcnt_barrier_rt<(NB - 2) * P::NIW>(later);
+    }
+    const int b = t % NB, b1 = b == NB - 1 ? 0 : b + 1, b2 = b == 0 ? NB - 1 : b - 1;
+    const int bv = b >= 2 ? b - 2 : b + NB - 2;
+    if (t + NB < n) issue_k(t + NB, b);
+    if (t + NB - 2 < n) issue_v(t + NB - 2, bv);
     // The softmax depends on nothing produced in this iteration; an opaque
     // copy of the reference keeps the compiler from hoisting it above the
     // barrier, so it stays in the block it is meant to overlap.
@@ -1361,8 +835,6 @@ void attn_stream_fix_bf16(Bf16Args a) {
     if constexpr (HAS_NEXT) scores(b1, nx0, nx1);
     weights(mask_c, t * BN, cu0, cu1, nmt, pout);
     if constexpr (HAS_PV) pv(b2, pin);
-    if constexpr (HAS_NEXT && HAS_PV)
-      fix_sched<2 * (DK / 16), 8 * S::MT, 2 * (DK / 16) + 4 * S::MT + (S::kOnes ? 0 : 4)>();
   };
   using F = std::integral_constant<bool, false>;
   using T = std::integral_constant<bool, true>;
@@ -1374,7 +846,7 @@ void attn_stream_fix_bf16(Bf16Args a) {
     if (ragged) body(T{}, F{}, T{}, t, cu0, cu1, sA0, sA1, pin, pout);
     else body(T{}, F{}, F{}, t, cu0, cu1, sA0, sA1, pin, pout);
     vmcnt_barrier<0>();
-    pv(t % 3, pout);
+    pv(t % NB, pout);
   };
 
   if (n == 1) {
@@ -1617,27 +1089,15 @@ void attn_short_bf16(Bf16Args a) {
 #ifndef SDATTN_SHORT_TILES
 #define SDATTN_SHORT_TILES 1
 #endif
-#ifndef SDATTN_STREAM_DMA
-#define SDATTN_STREAM_DMA 1
-#endif
-#ifndef SDATTN_STREAM_PINGPONG
-#define SDATTN_STREAM_PINGPONG 0
-#endif
-#ifndef SDATTN_STREAM_FIX
-#define SDATTN_STREAM_FIX 1
-#endif
 #ifndef SDATTN_STREAM_FIX_MAX_DK
 #define SDATTN_STREAM_FIX_MAX_DK 64
 #endif
-constexpr bool kStreamPingPong = SDATTN_STREAM_PINGPONG != 0;
-constexpr bool kStreamFix = SDATTN_STREAM_FIX != 0;
 #ifndef SDATTN_STREAM_FIX_WAVES
 #define SDATTN_STREAM_FIX_WAVES 8
 #endif
-constexpr int kStreamFixMaxDk = SDATTN_STREAM_FIX_MAX_DK;
+constexpr int kStreamFixMaxDk = SDATTN_STREAM_FIX_MAX_DK;  // widest DK of the fixed-reference kernel
 constexpr int kStreamFixWaves = SDATTN_STREAM_FIX_WAVES;
-constexpr int kStreamWaves = SDATTN_STREAM_WAVES;
-constexpr bool kStreamDma = SDATTN_STREAM_DMA != 0;
+constexpr int kStreamWaves = SDATTN_STREAM_WAVES;          // rescaling streaming kernel
 constexpr int kShortWaves = SDATTN_SHORT_WAVES;
 constexpr int kShortTiles = SDATTN_SHORT_TILES;   // query tiles per wave (short kernel)
 
@@ -1655,48 +1115,27 @@ hipError_t launch_dk(const Bf16Args &base, int BH, bool short_path, bool out_f32
     else
       hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, false>),
                          dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
-  } else if (kStreamFix && DK <= kStreamFixMaxDk) {
-    if constexpr (DK <= kStreamFixMaxDk) {
-      constexpr int NW = kStreamFixWaves;
-      const int per_wg = NW * kQW;
-      a.qblocks = (a.Lq + per_wg - 1) / per_wg;
-      a.nwg = BH * a.qblocks;
-      if (out_f32)
-        hipLaunchKernelGGL((attn_stream_fix_bf16<DK, NW, true>), dim3(a.nwg), dim3(NW * kWave),
-                           0, stream, a);
-      else
-        hipLaunchKernelGGL((attn_stream_fix_bf16<DK, NW, false>), dim3(a.nwg), dim3(NW * kWave),
-                           0, stream, a);
-    }
-  } else if (kStreamPingPong && DK <= 160) {
-    const int per_wg = 8 * kQW;
+  } else if constexpr (DK <= kStreamFixMaxDk) {
+    constexpr int NW = kStreamFixWaves;
+    const int per_wg = NW * kQW;
     a.qblocks = (a.Lq + per_wg - 1) / per_wg;
     a.nwg = BH * a.qblocks;
     if (out_f32)
-      hipLaunchKernelGGL((attn_stream_pp_bf16<DK, true>), dim3(a.nwg), dim3(8 * kWave), 0,
-                         stream, a);
+      hipLaunchKernelGGL((attn_stream_fix_bf16<DK, NW, true>), dim3(a.nwg), dim3(NW * kWave),
+                         0, stream, a);
     else
-      hipLaunchKernelGGL((attn_stream_pp_bf16<DK, false>), dim3(a.nwg), dim3(8 * kWave), 0,
-                         stream, a);
+      hipLaunchKernelGGL((attn_stream_fix_bf16<DK, NW, false>), dim3(a.nwg), dim3(NW * kWave),
+                         0, stream, a);
   } else {
     const int per_wg = kStreamWaves * kQW;
     a.qblocks = (a.Lq + per_wg - 1) / per_wg;
     a.nwg = BH * a.qblocks;
-    if constexpr (kStreamDma) {
-      if (out_f32)
-        hipLaunchKernelGGL((attn_stream_dma_bf16<DK, kStreamWaves, true>),
-                           dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
-      else
-        hipLaunchKernelGGL((attn_stream_dma_bf16<DK, kStreamWaves, false>),
-                           dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
-    } else {
-      if (out_f32)
-        hipLaunchKernelGGL((attn_stream_bf16<DK, kStreamWaves, true>),
-                           dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
-      else
-        hipLaunchKernelGGL((attn_stream_bf16<DK, kStreamWaves, false>),
-                           dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
-    }
+    if (out_f32)
+      hipLaunchKernelGGL((attn_stream_dma_bf16<DK, kStreamWaves, true>),
+                         dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_stream_dma_bf16<DK, kStreamWaves, false>),
+                         dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
   }
   return hipGetLastError();
 }
