@@ -49,7 +49,9 @@ STEPS = {
 }
 for _n in WORKLOADS:
     if _n != "1":
-        STEPS[f"workload_{_n}"] = [(_n, "cross" if WORKLOADS[_n].kind == "cross" else "fwd")]
+        # the cross entry takes contexts up to the LDS-resident cap (128)
+        _w = WORKLOADS[_n]
+        STEPS[f"workload_{_n}"] = [(_n, "cross" if _w.kind == "cross" and _w.Lk <= 128 else "fwd")]
 
 
 def kernel_source_sha() -> str:

@@ -43,7 +43,7 @@ def oracle_full(name):
 # the workloads at full size
 
 
-@pytest.mark.parametrize("name", ["1", "2", "3", "4a", "4b", "4c", "4d"])
+@pytest.mark.parametrize("name", ["1", "2", "3", "4a", "4b", "4c", "4d", "6a", "6b"])
 def test_workload_parity(dev, name):
     import torch
     w = WORKLOADS[name]
@@ -56,7 +56,9 @@ def test_workload_parity(dev, name):
             say(f"workload {name} {entry} f32 max/mean err %.3e %.3e" % errors(got, want))
             assert_f32_gate(got, want, f"{name}/{entry}")
         return
-    entries = ["auto", "stream"] + (["cross"] if w.kind == "cross" else [])
+    import unet_attention_amd as sd
+    in_cap = w.Lk <= sd.sdattn_cross_max_ctx(w.d, sd.SDATTN_DTYPE_BF16)
+    entries = ["auto", "stream"] + (["cross"] if w.kind == "cross" and in_cap else [])
     outs = {}
     for entry in entries:
         say(f"workload {name} bf16->fp32 entry={entry} {w}")
@@ -309,15 +311,18 @@ def test_non_default_stream(dev):
 def test_errors_on_device(dev):
     import torch
     import unet_attention_amd as sd
-    q = torch.zeros(1, 1, 256, 40, dtype=torch.bfloat16, device=dev)
+    # q is large enough that K/V views of up to 512 rows at its start stay
+    # inside it (so the overlap check does not fire before the one tested)
+    q = torch.zeros(1, 1, 512, 40, dtype=torch.bfloat16, device=dev)
     out = torch.empty(1, 1, 256, 40, dtype=torch.bfloat16, device=dev)
     p = q.data_ptr()
     say("misaligned pointer on device")
     assert sd.sdattn_fwd(p + 2, p, p, out.data_ptr(), 1, 1, 63, 64, 40, 0.1, 1, None) == \
         sd.SDATTN_ERR_MISALIGNED
     assert sd.sdattn_fwd(p, p, p, p, 1, 1, 64, 64, 40, 0.1, 1, None) == sd.SDATTN_ERR_INVALID_ARG
-    assert sd.sdattn_cross_fwd(p, p, p, out.data_ptr(), 1, 1, 64, 129, 40, 0.1, 1, None) == \
+    cap = sd.sdattn_cross_max_ctx(40, 1)
+    assert sd.sdattn_cross_fwd(p, p, p, out.data_ptr(), 1, 1, 64, cap + 1, 40, 0.1, 1, None) == \
         sd.SDATTN_ERR_UNSUPPORTED
     with pytest.raises(sd.SdattnError):
-        sd.cross_fwd(q, torch.zeros(1, 1, 200, 40, dtype=torch.bfloat16, device=dev),
-                     torch.zeros(1, 1, 200, 40, dtype=torch.bfloat16, device=dev))
+        sd.cross_fwd(q, torch.zeros(1, 1, cap + 1, 40, dtype=torch.bfloat16, device=dev),
+                     torch.zeros(1, 1, cap + 1, 40, dtype=torch.bfloat16, device=dev))

@@ -38,7 +38,11 @@ namespace sdattn {
 
 namespace {
 
-constexpr int kShortMax = 128;  // keys held by the short-key kernel
+// Keys held by the short-key kernel.  A 256-key instantiation (scores of all
+// keys in registers beside O) measured slower than the streaming kernels
+// beyond 128 keys for every head dim, so longer contexts stream.
+template <int DK>
+constexpr int short_cap() { return 128; }
 constexpr uint16_t kBf16One = 0x3F80;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer, range checked
 
@@ -65,14 +69,10 @@ struct Shape {
 
 // Two waves per SIMD keep the whole working set in <= 256 VGPRs (VGPR-form
 // MFMA); the widest head dims need more registers and run one wave per SIMD.
+// (The second __launch_bounds__ argument is this minimum waves per SIMD.)
 template <int DK>
 constexpr int waves_per_simd() { return DK <= 112 ? 2 : 1; }
 
-// Minimum resident workgroups per CU that gives waves_per_simd() (4 SIMDs).
-template <int DK, int NW>
-constexpr int min_blocks() {
-  return (4 * waves_per_simd<DK>() / NW) > 0 ? 4 * waves_per_simd<DK>() / NW : 1;
-}
 
 // Q fragments: B operand of S^T = K Q^T.  Lane l holds query q0 + l%32 and
 // columns dk*16 + 8*(l/32) .. +7; rows past Lq and columns past d are zero.
@@ -333,7 +333,7 @@ struct DmaPlan {
 };
 
 template <int DK, int NW, bool OUT_F32>
-__global__ __launch_bounds__(NW * kWave, (min_blocks<DK, NW>()))
+__global__ __launch_bounds__(NW * kWave, (waves_per_simd<DK>()))
 void attn_stream_dma_bf16(Bf16Args a) {
   using S = Shape<DK>;
   using P = DmaPlan<DK, NW>;
@@ -623,7 +623,7 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
 constexpr int kFixBuffers = SDATTN_FIX_BUFFERS;
 
 template <int DK, int NW, bool OUT_F32>
-__global__ __launch_bounds__(NW * kWave, 8 / NW)
+__global__ __launch_bounds__(NW * kWave, 2)
 void attn_stream_fix_bf16(Bf16Args a) {
   using S = Shape<DK>;
   using P = DmaPlan<DK, NW>;
@@ -892,7 +892,7 @@ void attn_stream_fix_bf16(Bf16Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Short-key kernel: Lk <= kShortMax, every key resident in LDS.
+// Short-key kernel: Lk <= KMAX (128 or 256), every key resident in LDS.
 
 // Epilogue through LDS: the wave writes its normalised 32 x d tile into a
 // private LDS region laid out exactly like the rows in HBM, then stores it
@@ -945,21 +945,21 @@ __device__ __forceinline__ void store_out_staged(const f32x16 (&o)[Shape<DK>::MT
         *reinterpret_cast<const u32x4 *>(stage + ch * 16);
 }
 
-template <int DK, int NW, int QPW, bool OUT_F32>
-__global__ __launch_bounds__(NW * kWave, (min_blocks<DK, NW>()))
+template <int DK, int NW, int QPW, int KMAX, bool OUT_F32>
+__global__ __launch_bounds__(NW * kWave, (waves_per_simd<DK>()))
 void attn_short_bf16(Bf16Args a) {
   using S = Shape<DK>;
   constexpr int NT = NW * kWave;
-  constexpr int NKT = kShortMax / 32;
-  constexpr int VST = kShortMax + 8;
-  constexpr int KCH = (kShortMax * S::DK8 + NT - 1) / NT;        // K chunks / thread
-  constexpr int VCH = ((kShortMax / 4) * S::DK8 + NT - 1) / NT;  // V units / thread
+  constexpr int NKT = KMAX / 32;
+  constexpr int VST = KMAX + 8;
+  constexpr int KCH = (KMAX * S::DK8 + NT - 1) / NT;        // K chunks / thread
+  constexpr int VCH = ((KMAX / 4) * S::DK8 + NT - 1) / NT;  // V units / thread
   constexpr int STAGE = kQW * DK * (OUT_F32 ? 4 : 2);            // bytes per wave
   // Output staging only where K, V^T and the staging area fit in half of the
   // CU's LDS (two workgroups per CU); otherwise rows are stored directly.
-  constexpr int KV_BYTES = (kShortMax * S::KST + S::DV * VST) * 2;
+  constexpr int KV_BYTES = (KMAX * S::KST + S::DV * VST) * 2;
   constexpr bool kStaged = KV_BYTES + NW * STAGE <= 80 * 1024;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kShortMax * S::KST];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KMAX * S::KST];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[S::DV * VST];
   __shared__ __attribute__((aligned(16))) uint8_t Ost[kStaged ? NW * STAGE : 16];
 
@@ -991,7 +991,7 @@ void attn_short_bf16(Bf16Args a) {
 #pragma unroll
   for (int t = 0; t < VCH; ++t) {
     const int u = tid + t * NT;
-    const int g = u % (kShortMax / 4), ch = u / (kShortMax / 4);
+    const int g = u % (KMAX / 4), ch = u / (KMAX / 4);
     if (g < ngroups && ch < d8) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -999,8 +999,8 @@ void attn_short_bf16(Bf16Args a) {
     }
   }
 
-  init_k_pad<DK, kShortMax>(Ks, d, tid, NT);
-  init_vt_const<DK, kShortMax>(Vt, VST, d, tid, NT);
+  init_k_pad<DK, KMAX>(Ks, d, tid, NT);
+  init_vt_const<DK, KMAX>(Vt, VST, d, tid, NT);
 #pragma unroll
   for (int t = 0; t < KCH; ++t) {
     const int idx = tid + t * NT;
@@ -1010,7 +1010,7 @@ void attn_short_bf16(Bf16Args a) {
 #pragma unroll
   for (int t = 0; t < VCH; ++t) {
     const int u = tid + t * NT;
-    const int g = u % (kShortMax / 4), ch = u / (kShortMax / 4);
+    const int g = u % (KMAX / 4), ch = u / (KMAX / 4);
     if (g < ngroups && ch < d8) store_vt_unit(Vt, VST, ch * 8, g, vreg[t]);
   }
   __syncthreads();
@@ -1109,12 +1109,23 @@ hipError_t launch_dk(const Bf16Args &base, int BH, bool short_path, bool out_f32
     const int per_wg = kShortWaves * kQW * kShortTiles;
     a.qblocks = (a.Lq + per_wg - 1) / per_wg;
     a.nwg = BH * a.qblocks;
-    if (out_f32)
-      hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, true>),
-                         dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, false>),
-                         dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
+    if (a.Lk <= 128) {
+      if (out_f32)
+        hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, 128, true>),
+                           dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, 128, false>),
+                           dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
+    } else if constexpr (short_cap<DK>() > 128) {
+      if (out_f32)
+        hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, 256, true>),
+                           dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, 256, false>),
+                           dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
+    } else {
+      return hipErrorInvalidValue;  // the API checks Lk against the cap first
+    }
   } else if constexpr (DK <= kStreamFixMaxDk) {
     constexpr int NW = kStreamFixWaves;
     const int per_wg = NW * kQW;
@@ -1142,7 +1153,10 @@ hipError_t launch_dk(const Bf16Args &base, int BH, bool short_path, bool out_f32
 
 }  // namespace
 
-int short_path_max_keys() { return kShortMax; }
+int short_path_max_keys(int d) {
+  (void)d;
+  return short_cap<16>();
+}
 
 hipError_t launch_bf16(const Bf16Args &a, int BH, bool short_path, bool out_f32,
                        hipStream_t stream) {

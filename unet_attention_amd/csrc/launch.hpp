@@ -8,8 +8,9 @@
 
 namespace sdattn {
 
-// Largest key count the short-key (all keys in LDS) bf16 kernel takes.
-int short_path_max_keys();
+// Largest key count the short-key (all keys in LDS) bf16 kernel takes for
+// head dimension d.
+int short_path_max_keys(int d);
 
 // bf16 kernels.  a.qblocks and a.nwg are filled in by the launcher.
 hipError_t launch_bf16(const Bf16Args &a, int BH, bool short_path, bool out_f32,

@@ -81,7 +81,7 @@ int run(const void *q, const void *k, const void *v, void *out, int B, int H,
         int Lq, int Lk, int d, float scale, int dtype, void *stream, Path path) {
   int rc = validate(q, k, v, out, B, H, Lq, Lk, d, scale, dtype);
   if (rc != SDATTN_OK) return rc;
-  const int cap = sdattn::short_path_max_keys();
+  const int cap = sdattn::short_path_max_keys(d);
   if (path == Path::Short && Lk > cap) return SDATTN_ERR_UNSUPPORTED;
   rc = check_device();
   if (rc != SDATTN_OK) return rc;
@@ -146,7 +146,7 @@ int sdattn_cross_max_ctx(int d, int dtype) {
       dtype != SDATTN_DTYPE_BF16_F32OUT)
     return 0;
   if (d < 8 || d > 256 || d % 8 != 0) return 0;
-  return sdattn::short_path_max_keys();
+  return sdattn::short_path_max_keys(d);
 }
 
 const char *sdattn_strerror(int status) {

@@ -88,6 +88,12 @@ WORKLOADS = {
     "5": Workload("5", "self", 8, 10, 16384, 16384, 64, "bf16", 5000,
                   heavy_frac=0.01, heavy_mult=8.0,
                   note="self-attention, 128x128 latent, 1% of keys x8"),
+    # Longer text contexts than CLIP's 77 tokens (several concatenated prompt
+    # chunks, or larger text encoders), 64x64 latent.
+    "6a": Workload("6a", "cross", 2, 8, 4096, 256, 40, "bf16", 6001,
+                   note="cross-attention, 64x64 latent, 256-token context"),
+    "6b": Workload("6b", "cross", 2, 8, 4096, 512, 40, "bf16", 6002,
+                   note="cross-attention, 64x64 latent, 512-token context"),
 }
 
 
