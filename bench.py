@@ -5,12 +5,13 @@ One step = the attention of one SD-1.5 transformer block at a 64x64 latent
 (512x512 image, classifier-free-guidance batch 2): self-attention
 B=2, H=8, Lq=Lk=4096, d=40 (streaming kernel) followed by cross-attention to
 the 77-token text context, B=2, H=8, Lq=4096, Lk=77, d=40 (short-key kernel).
-bf16 inputs and outputs, fp32 accumulation; inputs are seeded N(0,1)
-synthetic tensors resident in HBM before timing starts.
+bf16 inputs and outputs (fp16 for the *_f16 step), fp32 accumulation;
+inputs are seeded N(0,1) synthetic tensors resident in HBM before timing
+starts.
 
 Metric: attention TFLOP/s = 4*B*H*Lq*Lk*d summed over the step's calls,
 divided by the step time.  The JSON line also carries the roofline fraction
-of the dominant kernel (self-attention vs the bf16 dense MFMA peak, per-launch
+of the dominant kernel (self-attention vs the 16-bit dense MFMA peak, per-launch
 duration from HIP events recorded around each launch on its stream), the
 cross-attention kernel's HBM fraction, and the CPU oracle timed on the host.
 
@@ -38,7 +39,7 @@ if ROOT not in sys.path:
 
 from workloads import WORKLOADS, make_inputs  # noqa: E402
 
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 (and fp16) MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 ROTATE_BYTES = 640 << 20       # > 2x the 256 MB Infinity Cache
 METRIC = "attention TFLOP/s (4·B·H·Lq·Lk·d) and % of MI355X MFMA/HBM roofline"
@@ -46,6 +47,7 @@ METRIC = "attention TFLOP/s (4·B·H·Lq·Lk·d) and % of MI355X MFMA/HBM roofli
 # Step definitions: name -> list of (workload, entry point).
 STEPS = {
     "sd15_64x64_block": [("2", "fwd"), ("3", "cross")],
+    "sd15_64x64_block_f16": [("2h", "fwd"), ("3h", "cross")],
 }
 for _n in WORKLOADS:
     if _n != "1":
@@ -128,11 +130,15 @@ def main():
     ws = [WORKLOADS[n] for n, _ in calls]
     inputs = [make_inputs(w) for w in ws]
 
-    def dev_bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
-            torch.bfloat16).to(dev)
+    elt = ws[0].dtype  # "bf16" or "f16"; one element type per step
+    assert all(w.dtype == elt for w in ws) and elt in ("bf16", "f16")
+    tdt = torch.bfloat16 if elt == "bf16" else torch.float16
+    dtype_code = sd.SDATTN_DTYPE_BF16 if elt == "bf16" else sd.SDATTN_DTYPE_F16
 
-    base = [tuple(dev_bf16(b) for b in (x.q_bits, x.k_bits, x.v_bits)) for x in inputs]
+    def dev16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
+
+    base = [tuple(dev16(b) for b in (x.q_bits, x.k_bits, x.v_bits)) for x in inputs]
     set_bytes = sum(2 * (q.numel() + k.numel() + v.numel() + q.numel()) for q, k, v in base)
     nsets = max(2, -(-ROTATE_BYTES // set_bytes))
     sets = []
@@ -152,7 +158,7 @@ def main():
         for (n, entry), w, (q, k, v, o) in zip(calls, ws, sets[s]):
             row.append((fns[entry], (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                      w.B, w.H, w.Lq, w.Lk, w.d, w.scale,
-                                     sd.SDATTN_DTYPE_BF16, sh)))
+                                     dtype_code, sh)))
         argv.append(row)
 
     def launch(fn, a):
@@ -246,10 +252,10 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": elt, "data": "synthetic",
         "config": {"workload": args.workload,
                    "calls": [f"{k['entry']} {k['shape']}" for k in kernels],
-                   "io": "bf16 in/out, fp32 accumulation",
+                   "io": f"{elt} in/out, fp32 accumulation",
                    "buffer_sets_rotated": nsets,
                    "rotated_bytes": nsets * set_bytes},
         "roofline": roof,

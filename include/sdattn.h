@@ -27,6 +27,13 @@
  *                             the softmax weights are rounded to bf16 before
  *                             the second product.
  *   SDATTN_DTYPE_BF16_F32OUT  as SDATTN_DTYPE_BF16 but out is fp32.
+ *   SDATTN_DTYPE_F16          fp16 q/k/v, fp16 out: the half-precision
+ *                             storage the same page's section 5.2 uses for
+ *                             weights and activations; fp16 matrix products
+ *                             with fp32 accumulation, weights rounded to fp16
+ *                             (kept <= 2^8 by the running maximum, well
+ *                             inside fp16's range).
+ *   SDATTN_DTYPE_F16_F32OUT   as SDATTN_DTYPE_F16 but out is fp32.
  *
  * Ownership and synchronisation.  The caller owns every buffer and the
  * stream.  The library allocates no device memory and needs no workspace.
@@ -63,7 +70,9 @@ typedef enum {
 typedef enum {
   SDATTN_DTYPE_F32 = 0,
   SDATTN_DTYPE_BF16 = 1,
-  SDATTN_DTYPE_BF16_F32OUT = 2
+  SDATTN_DTYPE_BF16_F32OUT = 2,
+  SDATTN_DTYPE_F16 = 3,
+  SDATTN_DTYPE_F16_F32OUT = 4
 } sdattn_dtype;
 
 /* Attention with any key length.  Internally dispatches to the short-key

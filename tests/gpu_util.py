@@ -22,9 +22,10 @@ def say(msg: str) -> None:
 def to_device(x, device="cuda"):
     """Inputs -> (q, k, v) torch tensors holding exactly the stored values."""
     import torch
-    if x.w.dtype == "bf16":
+    if x.w.dtype in ("bf16", "f16"):
+        tdt = torch.bfloat16 if x.w.dtype == "bf16" else torch.float16
         cv = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(
-            torch.bfloat16).to(device)
+            tdt).to(device)
         return cv(x.q_bits), cv(x.k_bits), cv(x.v_bits)
     return tuple(torch.from_numpy(np.ascontiguousarray(t)).to(device) for t in (x.q, x.k, x.v))
 
@@ -36,6 +37,9 @@ def tensors_from_f32(q, k, v, dtype: str, device="cuda"):
     if dtype == "bf16":
         cv = lambda a: torch.from_numpy(round_to_bf16_bits(a).view(np.int16)).view(
             torch.bfloat16).to(device)
+        return cv(q), cv(k), cv(v)
+    if dtype == "f16":
+        cv = lambda a: torch.from_numpy(np.ascontiguousarray(a).astype(np.float16)).to(device)
         return cv(q), cv(k), cv(v)
     return tuple(torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
                  for a in (q, k, v))
@@ -76,10 +80,18 @@ def half_ulp_bf16(x):
     return np.where(x == 0, 0.0, np.ldexp(1.0, e - 9))
 
 
-def assert_bf16_out_gate(got, want, what=""):
-    """bf16 output adds its own rounding: allow half a bf16 ulp of the exact
-    value on top of the bf16 gate, elementwise and on the mean."""
-    h = half_ulp_bf16(want)
+def half_ulp_f16(x):
+    """Half an fp16 unit in the last place (11 significant bits; subnormal
+    spacing 2^-24 below 2^-14)."""
+    m, e = np.frexp(np.abs(x))
+    return np.where(x == 0, 0.0, np.maximum(np.ldexp(1.0, e - 12), 2.0 ** -25))
+
+
+def assert_bf16_out_gate(got, want, what="", out="bf16"):
+    """A 16-bit output adds its own rounding: allow half an ulp of the output
+    type (bf16 or fp16) of the exact value on top of the bf16 gate,
+    elementwise and on the mean."""
+    h = half_ulp_bf16(want) if out == "bf16" else half_ulp_f16(want)
     e = np.abs(got - want)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     worst = float((e - h).max())

@@ -38,7 +38,7 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert sd.sdattn_version() == 10000
+    assert sd.sdattn_version() == 10100
     seen = set()
     for code in range(6):
         msg = sd.sdattn_strerror(code)
@@ -49,11 +49,13 @@ def test_version_and_strerror(lib):
 
 
 def test_cross_max_ctx(lib):
-    for dt in (sd.SDATTN_DTYPE_F32, sd.SDATTN_DTYPE_BF16, sd.SDATTN_DTYPE_BF16_F32OUT):
+    for dt in (sd.SDATTN_DTYPE_F32, sd.SDATTN_DTYPE_BF16, sd.SDATTN_DTYPE_BF16_F32OUT,
+               sd.SDATTN_DTYPE_F16, sd.SDATTN_DTYPE_F16_F32OUT):
         for d in (8, 40, 64, 80, 160, 256):
             assert sd.sdattn_cross_max_ctx(d, dt) >= 77
         for d in (0, 4, 41, 264, -8):
             assert sd.sdattn_cross_max_ctx(d, dt) == 0
+    assert sd.sdattn_cross_max_ctx(40, 5) == 0
     assert sd.sdattn_cross_max_ctx(40, 7) == 0
 
 
@@ -80,7 +82,7 @@ BAD = [
     ("Lk0", dict(Lk=0), sd.SDATTN_ERR_INVALID_ARG),
     ("d0", dict(d=0), sd.SDATTN_ERR_INVALID_ARG),
     ("negB", dict(B=-1), sd.SDATTN_ERR_INVALID_ARG),
-    ("dtype", dict(dtype=3), sd.SDATTN_ERR_INVALID_ARG),
+    ("dtype", dict(dtype=5), sd.SDATTN_ERR_INVALID_ARG),
     ("dtype_neg", dict(dtype=-1), sd.SDATTN_ERR_INVALID_ARG),
     ("nan_scale", dict(scale=float("nan")), sd.SDATTN_ERR_INVALID_ARG),
     ("inf_scale", dict(scale=float("inf")), sd.SDATTN_ERR_INVALID_ARG),
@@ -105,7 +107,7 @@ def test_invalid_arguments(lib, entry, case):
     assert call(entry, **kw) == want
 
 
-@pytest.mark.parametrize("dtype", [0, 1, 2])
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3, 4])
 def test_cross_rejects_long_context(lib, dtype):
     cap = sd.sdattn_cross_max_ctx(40, dtype)
     assert call("sdattn_cross_fwd", Lk=cap + 1, dtype=dtype) == sd.SDATTN_ERR_UNSUPPORTED
@@ -117,10 +119,11 @@ def _gpu_present():
 
 
 @pytest.mark.parametrize("entry", ENTRIES)
-def test_valid_call_without_gpu_reports_device(lib, entry):
+@pytest.mark.parametrize("dtype", [1, 2, 3, 4])
+def test_valid_call_without_gpu_reports_device(lib, entry, dtype):
     if _gpu_present():
         pytest.skip("a GPU is present; fake pointers must not reach a launch")
-    assert call(entry) == sd.SDATTN_ERR_DEVICE
+    assert call(entry, dtype=dtype) == sd.SDATTN_ERR_DEVICE
 
 
 def test_torch_wrapper_checks_shapes(lib):

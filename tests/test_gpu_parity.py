@@ -43,7 +43,7 @@ def oracle_full(name):
 # the workloads at full size
 
 
-@pytest.mark.parametrize("name", ["1", "2", "3", "4a", "4b", "4c", "4d", "6a", "6b"])
+@pytest.mark.parametrize("name", ["1", "2", "3", "4a", "4b", "4c", "4d", "6a", "6b", "2h", "3h"])
 def test_workload_parity(dev, name):
     import torch
     w = WORKLOADS[name]
@@ -65,20 +65,23 @@ def test_workload_parity(dev, name):
         outs[entry] = got = run(entry, q, k, v, w.scale, out_dtype=torch.float32)
         say(f"workload {name} {entry} f32out max/mean err %.3e %.3e" % errors(got, want))
         assert_bf16_gate(got, want, f"{name}/{entry}/f32out")
-        say(f"workload {name} bf16->bf16 entry={entry}")
-        gotb = run(entry, q, k, v, w.scale, out_dtype=torch.bfloat16)
-        say(f"workload {name} {entry} bf16out max/mean err %.3e %.3e" % errors(gotb, want))
-        assert_bf16_out_gate(gotb, want, f"{name}/{entry}/bf16out")
+        lo = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+        say(f"workload {name} {w.dtype}->{w.dtype} entry={entry}")
+        gotb = run(entry, q, k, v, w.scale, out_dtype=lo)
+        say(f"workload {name} {entry} {w.dtype} out max/mean err %.3e %.3e" % errors(gotb, want))
+        assert_bf16_out_gate(gotb, want, f"{name}/{entry}/{w.dtype}out", out=w.dtype)
     if "cross" in outs:
         assert np.array_equal(outs["cross"], outs["auto"]), "cross entry != fwd entry"
 
 
-def test_workload5_sampled(dev):
-    """128x128 latent, B=8, H=10, L=16384, d=64, 1% of keys x8: full-size GPU
-    run in the benchmark's launch configuration, checked on sampled rows that
-    cover every (b, h), tile edges and the last rows."""
+@pytest.mark.parametrize("name", ["5", "5h"])
+def test_workload5_sampled(dev, name):
+    """128x128 latent, B=8, H=10, L=16384, d=64, 1% of keys x8 (bf16, and
+    fp16 as 5h): full-size GPU run in the benchmark's launch configuration,
+    checked on sampled rows that cover every (b, h), tile edges and the last
+    rows."""
     import torch
-    w = WORKLOADS["5"]
+    w = WORKLOADS[name]
     x = make_inputs(w)
     rows = sample_rows(w, 1024)
     want = oracle.attn_rows(x.q, x.k, x.v, w.scale, rows)
@@ -86,14 +89,16 @@ def test_workload5_sampled(dev):
     del x
     import unet_attention_amd as sd
     idx = torch.from_numpy(rows).to(dev)
-    for odt, gate in ((torch.float32, assert_bf16_gate), (torch.bfloat16, assert_bf16_out_gate)):
-        say(f"workload 5 full size, out {odt}, {rows.size} sampled rows")
+    lo = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    gate_lo = lambda g, t, what: assert_bf16_out_gate(g, t, what, out=w.dtype)
+    for odt, gate in ((torch.float32, assert_bf16_gate), (lo, gate_lo)):
+        say(f"workload {name} full size, out {odt}, {rows.size} sampled rows")
         out = sd.fwd(q, k, v, scale=w.scale, out_dtype=odt)
         torch.cuda.synchronize()
         assert bool(torch.isfinite(out).all()), "non-finite output"
         got = out.view(-1, w.d)[idx].float().cpu().numpy().astype(np.float64)
-        say(f"workload 5 out {odt} max/mean err %.3e %.3e" % errors(got, want))
-        gate(got, want, f"5/{odt}")
+        say(f"workload {name} out {odt} max/mean err %.3e %.3e" % errors(got, want))
+        gate(got, want, f"{name}/{odt}")
         del out
 
 
@@ -124,6 +129,26 @@ def test_ragged_bf16(dev, Lq, Lk, d):
         assert_bf16_gate(got, want, f"Lq={Lq} Lk={Lk} d={d} {entry}")
         gotb = run(entry, q, k, v, w.scale, out_dtype=torch.bfloat16)
         assert_bf16_out_gate(gotb, want, f"Lq={Lq} Lk={Lk} d={d} {entry} bf16out")
+
+
+@pytest.mark.parametrize("d", [8, 40, 64, 80, 160, 256])
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (33, 63), (17, 77), (64, 128), (31, 129), (100, 333)])
+def test_ragged_f16(dev, Lq, Lk, d):
+    import torch
+    import unet_attention_amd as sd
+    w = Workload("ragged16", "self", 1, 2, Lq, Lk, d, "f16", 9000 + 31 * Lq + Lk + d)
+    x = make_inputs(w)
+    want = oracle.attn(x.q, x.k, x.v, w.scale)
+    q, k, v = to_device(x)
+    entries = ["auto", "stream"]
+    if Lk <= sd.sdattn_cross_max_ctx(d, sd.SDATTN_DTYPE_F16):
+        entries.append("cross")
+    for entry in entries:
+        say(f"ragged f16 Lq={Lq} Lk={Lk} d={d} entry={entry}")
+        got = run(entry, q, k, v, w.scale, out_dtype=torch.float32)
+        assert_bf16_gate(got, want, f"f16 Lq={Lq} Lk={Lk} d={d} {entry}")
+        goth = run(entry, q, k, v, w.scale, out_dtype=torch.float16)
+        assert_bf16_out_gate(goth, want, f"f16 Lq={Lq} Lk={Lk} d={d} {entry} f16out", out="f16")
 
 
 @pytest.mark.parametrize("d", [8, 40, 64, 200, 256])
@@ -235,9 +260,10 @@ def test_shifted_keys_stress_running_max(dev):
     assert_bf16_gate(run("auto", tq, tk, tv, 0.125, torch.float32), want, "shifted keys")
 
 
-def _aligned_key_case(d, seed, v_big=None):
+def _aligned_key_case(d, seed, v_big=None, dtype="bf16"):
     """Every query close to one direction u (|q| ~ 6); key 250 = 24 u, the
-    other keys small: key 250 scores ~144 above the rest (times scale)."""
+    other keys small: key 250 scores ~144 above the rest (times scale).
+    Values are rounded to `dtype` (bf16 or f16)."""
     from workloads import bf16_bits_to_f32, round_to_bf16_bits
     Lq, Lk, jstar = 70, 333, 250
     u = np.full(d, 1.0 / math.sqrt(d), dtype=np.float32)
@@ -247,24 +273,27 @@ def _aligned_key_case(d, seed, v_big=None):
     v = _rand((1, 2, Lk, d), seed + 2)
     if v_big is not None:
         v[:, :, jstar] = v_big
+    if dtype == "f16":
+        return tuple(a.astype(np.float16).astype(np.float32) for a in (q, k, v))
     return tuple(bf16_bits_to_f32(round_to_bf16_bits(a)) for a in (q, k, v))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [40, 64, 80])
 @pytest.mark.parametrize("scale", [1.0, 0.5])
-def test_far_key_beyond_first_tile(dev, d, scale):
+def test_far_key_beyond_first_tile(dev, d, scale, dtype):
     """A key whose score exceeds every score of the first key tile by ~200
     (scale 1) or ~100 (scale 0.5) binary orders: weights taken relative to an
     early maximum overflow fp32 in the first case, and must still give the
     oracle's result."""
     import torch
-    q, k, v = _aligned_key_case(d, 300 + d)
+    q, k, v = _aligned_key_case(d, 300 + d, dtype=dtype)
     want = oracle.attn(q, k, v, scale)
-    tq, tk, tv = tensors_from_f32(q, k, v, "bf16")
+    tq, tk, tv = tensors_from_f32(q, k, v, dtype)
     for entry in ("auto", "stream"):
-        say(f"far key d={d} scale={scale} {entry}")
+        say(f"far key {dtype} d={d} scale={scale} {entry}")
         got = run(entry, tq, tk, tv, scale, torch.float32)
-        assert_bf16_gate(got, want, f"far key d={d} scale={scale} {entry}")
+        assert_bf16_gate(got, want, f"far key {dtype} d={d} scale={scale} {entry}")
 
 
 @pytest.mark.parametrize("d", [40, 64])

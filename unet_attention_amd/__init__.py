@@ -29,6 +29,8 @@ SDATTN_ERR_LAUNCH = 5
 SDATTN_DTYPE_F32 = 0
 SDATTN_DTYPE_BF16 = 1
 SDATTN_DTYPE_BF16_F32OUT = 2
+SDATTN_DTYPE_F16 = 3
+SDATTN_DTYPE_F16_F32OUT = 4
 
 # Every function the C header declares, with its ctypes signature.
 _VP = ctypes.c_void_p
@@ -118,6 +120,14 @@ def _call(entry, q, k, v, out=None, scale=None, out_dtype=None, stream=None):
             dtype_code = SDATTN_DTYPE_BF16
         elif odt == torch.float32:
             dtype_code = SDATTN_DTYPE_BF16_F32OUT
+        else:
+            raise ValueError(f"unsupported output dtype {odt}")
+    elif q.dtype == torch.float16:
+        odt = out_dtype or torch.float16
+        if odt == torch.float16:
+            dtype_code = SDATTN_DTYPE_F16
+        elif odt == torch.float32:
+            dtype_code = SDATTN_DTYPE_F16_F32OUT
         else:
             raise ValueError(f"unsupported output dtype {odt}")
     else:

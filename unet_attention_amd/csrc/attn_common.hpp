@@ -22,9 +22,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // exact arithmetic because l and O always share the same stale m.
 constexpr float kRescaleSlack = 8.0f;
 
-// Arguments common to the bf16 kernels.  Pointers are [B, H, L, d]
-// contiguous; q/k/v hold bf16 bit patterns.
-struct Bf16Args {
+// Arguments common to the 16-bit (bf16 or fp16) kernels.  Pointers are
+// [B, H, L, d] contiguous; q/k/v hold 16-bit element bit patterns.
+struct Args16 {
   const uint16_t *q;
   const uint16_t *k;
   const uint16_t *v;
@@ -63,6 +63,24 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+// The 16-bit element type of the matrix-core kernels: bf16 (H = false) or
+// fp16 (H = true).  Operands travel as bit patterns in bf16x8 containers;
+// only the matrix instruction, the packing of fp32 results and the constant
+// one differ.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <bool H>
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (H)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool H>
+constexpr uint16_t one16() { return H ? 0x3C00 : 0x3F80; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) {
   return __builtin_bit_cast(bf16x8, x);
@@ -116,6 +134,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 p = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// Same in the element type H (fp16: v_cvt_pk_f16_f32, round to nearest even).
+template <bool H>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (H) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 p = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, p);
+  } else {
+    return pack_bf16x2(lo, hi);
+  }
 }
 
 }  // namespace sdattn

@@ -43,7 +43,6 @@ namespace {
 // beyond 128 keys for every head dim, so longer contexts stream.
 template <int DK>
 constexpr int short_cap() { return 128; }
-constexpr uint16_t kBf16One = 0x3F80;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer, range checked
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -112,7 +111,7 @@ __device__ __forceinline__ void store_vt_unit(uint16_t *vt, int vst, int row0,
 
 // Rows [d, DV) of V^T never change: zeros, plus a row of ones at d when the
 // row sum is taken from the matrix core.  KEYS slots per row are written.
-template <int DK, int KEYS>
+template <int DK, int KEYS, bool H = false>
 __device__ __forceinline__ void init_vt_const(uint16_t *vt, int vst, int d, int tid,
                                               int nthreads) {
   using S = Shape<DK>;
@@ -120,7 +119,7 @@ __device__ __forceinline__ void init_vt_const(uint16_t *vt, int vst, int d, int 
   const int n = (S::DV - d) * per_row;
   for (int idx = tid; idx < n; idx += nthreads) {
     const int r = d + idx / per_row, c8 = idx % per_row;
-    const uint32_t w = (S::kOnes && r == d) ? (uint32_t(kBf16One) * 0x10001u) : 0u;
+    const uint32_t w = (S::kOnes && r == d) ? (uint32_t(one16<H>()) * 0x10001u) : 0u;
     st16(vt + r * vst + c8 * 8, u32x4{w, w, w, w});
   }
 }
@@ -136,23 +135,23 @@ __device__ __forceinline__ void init_k_pad(uint16_t *ks, int d, int tid, int nth
 }
 
 // One 32-key sub-tile of S^T for this wave: sum over head-dim chunks.
-template <int DK>
+template <int DK, bool H = false>
 __device__ __forceinline__ f32x16 scores_subtile(const uint16_t *kp,
                                                  const bf16x8 (&qf)[DK / 16]) {
   f32x16 acc = {};
 #pragma unroll
   for (int dk = 0; dk < DK / 16; ++dk)
-    acc = mfma32x32x16(as_bf16x8(ld16(kp + dk * 16)), qf[dk], acc);
+    acc = mma<H>(as_bf16x8(ld16(kp + dk * 16)), qf[dk], acc);
   return acc;
 }
 
 // O^T += V^T P^T over one 16-key chunk; vp points at this lane's row/slot.
-template <int DK>
+template <int DK, bool H = false>
 __device__ __forceinline__ void pv_chunk(f32x16 (&o)[Shape<DK>::MT],
                                          const uint16_t *vp, int vst, bf16x8 p) {
 #pragma unroll
   for (int mt = 0; mt < Shape<DK>::MT; ++mt)
-    o[mt] = mfma32x32x16(as_bf16x8(ld16(vp + mt * 32 * vst)), p, o[mt]);
+    o[mt] = mma<H>(as_bf16x8(ld16(vp + mt * 32 * vst)), p, o[mt]);
 }
 
 // Key index (relative to the sub-tile) of accumulator register i in this lane.
@@ -168,7 +167,7 @@ __device__ __forceinline__ float max16(const f32x16 &s, float m) {
 }
 
 // Epilogue: divide by the row sum l and store this wave's 32 rows.
-template <int DK, bool OUT_F32>
+template <int DK, bool OUT_F32, bool H = false>
 __device__ __forceinline__ void store_out_l(const f32x16 (&o)[Shape<DK>::MT], float l,
                                             void *outp, size_t obase, int q0, int Lq,
                                             int d, int lane) {
@@ -190,7 +189,7 @@ __device__ __forceinline__ void store_out_l(const f32x16 (&o)[Shape<DK>::MT], fl
           f32x4 x = {x0, x1, x2, x3};
           *reinterpret_cast<f32x4 *>(static_cast<float *>(outp) + off) = x;
         } else {
-          u32x2 x = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+          u32x2 x = {pack2<H>(x0, x1), pack2<H>(x2, x3)};
           *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(outp) + off) = x;
         }
       }
@@ -199,7 +198,7 @@ __device__ __forceinline__ void store_out_l(const f32x16 (&o)[Shape<DK>::MT], fl
 
 // Same, with l taken from the ones row of O^T (padded head dims) or from the
 // per-lane partial sums lsum.
-template <int DK, bool OUT_F32>
+template <int DK, bool OUT_F32, bool H = false>
 __device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::MT],
                                           float lsum, void *outp, size_t obase,
                                           int q0, int Lq, int d, int lane) {
@@ -217,7 +216,7 @@ __device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::MT],
   } else {
     l = sum_halves(lsum);
   }
-  store_out_l<DK, OUT_F32>(o, l, outp, obase, q0, Lq, d, lane);
+  store_out_l<DK, OUT_F32, H>(o, l, outp, obase, q0, Lq, d, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -332,9 +331,9 @@ struct DmaPlan {
   static constexpr int NIW = (NI + NW - 1) / NW;    // per wave, upper bound
 };
 
-template <int DK, int NW, bool OUT_F32>
+template <int DK, int NW, bool OUT_F32, bool H>
 __global__ __launch_bounds__(NW * kWave, (waves_per_simd<DK>()))
-void attn_stream_dma_bf16(Bf16Args a) {
+void attn_stream_rescale(Args16 a) {
   using S = Shape<DK>;
   using P = DmaPlan<DK, NW>;
   constexpr int BN = P::BN, NSUB = P::NSUB;
@@ -408,7 +407,7 @@ void attn_stream_dma_bf16(Bf16Args a) {
   for (int idx = tid; idx < P::NB * BN * (S::DV / 8); idx += NW * kWave) {
     const int r = idx / (S::DV / 8), c8 = idx - r * (S::DV / 8);
     if (c8 >= d8) {
-      const uint32_t w0 = (S::kOnes && c8 == d8) ? uint32_t(kBf16One) : 0u;
+      const uint32_t w0 = (S::kOnes && c8 == d8) ? uint32_t(one16<H>()) : 0u;
       st16(Vs + r * P::VSTR + c8 * 8, u32x4{w0, 0u, 0u, 0u});
     }
   }
@@ -432,7 +431,7 @@ void attn_stream_dma_bf16(Bf16Args a) {
       const s16x4 lo = ld_tr16(vp), hi = ld_tr16(vp + 8 * P::VSTR);
       const bf16x8 av =
           __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[mt] = mfma32x32x16(av, pk, o[mt]);
+      o[mt] = mma<H>(av, pk, o[mt]);
     }
   };
 
@@ -470,8 +469,8 @@ void attn_stream_dma_bf16(Bf16Args a) {
         p[j] = x;
         if constexpr (!S::kOnes) lsum += x;
       }
-      const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+      const u32x4 pk = {pack2<H>(p[0], p[1]), pack2<H>(p[2], p[3]),
+                        pack2<H>(p[4], p[5]), pack2<H>(p[6], p[7])};
       pv(vb, kc0 + kk, as_bf16x8(pk));
     }
   };
@@ -490,8 +489,8 @@ void attn_stream_dma_bf16(Bf16Args a) {
     if (t + 2 < ntiles) issue(t + 2, (B + 2) % 3);
     const uint16_t *kb = Ks + B * P::KBUF + koff;
     const uint16_t *vb = Vs + B * P::VBUF;
-    f32x16 s0 = scores_subtile<DK>(kb, qf), s1;
-    if constexpr (NSUB == 2) s1 = scores_subtile<DK>(kb + 32 * S::KST, qf);
+    f32x16 s0 = scores_subtile<DK, H>(kb, qf), s1;
+    if constexpr (NSUB == 2) s1 = scores_subtile<DK, H>(kb + 32 * S::KST, qf);
     sub(mask_c, s0, t * BN, vb, 0);
     if constexpr (NSUB == 2) sub(mask_c, s1, t * BN + 32, vb, 2);
     if (t + 1 < ntiles) vmcnt_barrier_rt<P::NIW>(t + 2 < ntiles ? my_count : 0);
@@ -520,7 +519,7 @@ void attn_stream_dma_bf16(Bf16Args a) {
     step(B0{}, Ragged{}, t);
   }
 
-  store_out<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
+  store_out<DK, OUT_F32, H>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -624,7 +623,7 @@ constexpr int kFixBuffers = SDATTN_FIX_BUFFERS;
 
 template <int DK, int NW, bool OUT_F32>
 __global__ __launch_bounds__(NW * kWave, 2)
-void attn_stream_fix_bf16(Bf16Args a) {
+void attn_stream_fix(Args16 a) {
   using S = Shape<DK>;
   using P = DmaPlan<DK, NW>;
   static_assert(P::BN == 64 && P::NSUB == 2, "64-key tiles");
@@ -719,7 +718,7 @@ void attn_stream_fix_bf16(Bf16Args a) {
   for (int idx = tid; idx < NB * BN * (S::DV / 8); idx += NW * kWave) {
     const int r = idx / (S::DV / 8), c8 = idx - r * (S::DV / 8);
     if (c8 >= d8) {
-      const uint32_t w0 = (S::kOnes && c8 == d8) ? uint32_t(kBf16One) : 0u;
+      const uint32_t w0 = (S::kOnes && c8 == d8) ? uint32_t(one16<false>()) : 0u;
       st16(Vs + r * P::VSTR + c8 * 8, u32x4{w0, 0u, 0u, 0u});
     }
   }
@@ -897,7 +896,7 @@ void attn_stream_fix_bf16(Bf16Args a) {
 // Epilogue through LDS: the wave writes its normalised 32 x d tile into a
 // private LDS region laid out exactly like the rows in HBM, then stores it
 // with 16-byte contiguous chunks (whole cache lines per instruction).
-template <int DK, bool OUT_F32>
+template <int DK, bool OUT_F32, bool H = false>
 __device__ __forceinline__ void store_out_staged(const f32x16 (&o)[Shape<DK>::MT],
                                                  float lsum, void *outp, size_t obase,
                                                  int q0, int Lq, int d, int lane,
@@ -930,7 +929,7 @@ __device__ __forceinline__ void store_out_staged(const f32x16 (&o)[Shape<DK>::MT
         if constexpr (OUT_F32) {
           *reinterpret_cast<f32x4 *>(dst) = f32x4{x0, x1, x2, x3};
         } else {
-          *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+          *reinterpret_cast<u32x2 *>(dst) = u32x2{pack2<H>(x0, x1), pack2<H>(x2, x3)};
         }
       }
     }
@@ -945,9 +944,9 @@ __device__ __forceinline__ void store_out_staged(const f32x16 (&o)[Shape<DK>::MT
         *reinterpret_cast<const u32x4 *>(stage + ch * 16);
 }
 
-template <int DK, int NW, int QPW, int KMAX, bool OUT_F32>
+template <int DK, int NW, int QPW, int KMAX, bool OUT_F32, bool H>
 __global__ __launch_bounds__(NW * kWave, (waves_per_simd<DK>()))
-void attn_short_bf16(Bf16Args a) {
+void attn_short(Args16 a) {
   using S = Shape<DK>;
   constexpr int NT = NW * kWave;
   constexpr int NKT = KMAX / 32;
@@ -1000,7 +999,7 @@ void attn_short_bf16(Bf16Args a) {
   }
 
   init_k_pad<DK, KMAX>(Ks, d, tid, NT);
-  init_vt_const<DK, KMAX>(Vt, VST, d, tid, NT);
+  init_vt_const<DK, KMAX, H>(Vt, VST, d, tid, NT);
 #pragma unroll
   for (int t = 0; t < KCH; ++t) {
     const int idx = tid + t * NT;
@@ -1029,7 +1028,7 @@ void attn_short_bf16(Bf16Args a) {
 #pragma unroll
     for (int nt = 0; nt < NKT; ++nt) {
       if (nt < nkt) {
-        s[nt] = scores_subtile<DK>(Ks + koff + nt * 32 * S::KST, qf);
+        s[nt] = scores_subtile<DK, H>(Ks + koff + nt * 32 * S::KST, qf);
         if (nt == nkt - 1) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
@@ -1061,17 +1060,17 @@ void attn_short_bf16(Bf16Args a) {
             p[j] = x;
             if constexpr (!S::kOnes) lsum += x;
           }
-          const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-          pv_chunk<DK>(o, Vt + voff + (nt * 2 + kk) * 16, VST, as_bf16x8(pk));
+          const u32x4 pk = {pack2<H>(p[0], p[1]), pack2<H>(p[2], p[3]),
+                            pack2<H>(p[4], p[5]), pack2<H>(p[6], p[7])};
+          pv_chunk<DK, H>(o, Vt + voff + (nt * 2 + kk) * 16, VST, as_bf16x8(pk));
         }
       }
     }
     if constexpr (kStaged)
-      store_out_staged<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane,
+      store_out_staged<DK, OUT_F32, H>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane,
                                     stage);
     else
-      store_out<DK, OUT_F32>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
+      store_out<DK, OUT_F32, H>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
     if (t + 1 < QPW) {
 #pragma unroll
       for (int dk = 0; dk < DK / 16; ++dk) qf[dk] = qn[dk];
@@ -1101,52 +1100,62 @@ constexpr int kStreamWaves = SDATTN_STREAM_WAVES;          // rescaling streamin
 constexpr int kShortWaves = SDATTN_SHORT_WAVES;
 constexpr int kShortTiles = SDATTN_SHORT_TILES;   // query tiles per wave (short kernel)
 
+template <int DK, bool H>
+void launch_short(Args16 a, int BH, bool out_f32, hipStream_t stream) {
+  constexpr int NW = kShortWaves, QPW = kShortTiles, KMAX = short_cap<DK>();
+  const int per_wg = NW * kQW * QPW;
+  a.qblocks = (a.Lq + per_wg - 1) / per_wg;
+  a.nwg = BH * a.qblocks;
+  if (out_f32)
+    hipLaunchKernelGGL((attn_short<DK, NW, QPW, KMAX, true, H>), dim3(a.nwg), dim3(NW * kWave),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_short<DK, NW, QPW, KMAX, false, H>), dim3(a.nwg),
+                       dim3(NW * kWave), 0, stream, a);
+}
+
+template <int DK, bool H>
+void launch_rescale(Args16 a, int BH, bool out_f32, hipStream_t stream) {
+  constexpr int NW = kStreamWaves;
+  a.qblocks = (a.Lq + NW * kQW - 1) / (NW * kQW);
+  a.nwg = BH * a.qblocks;
+  if (out_f32)
+    hipLaunchKernelGGL((attn_stream_rescale<DK, NW, true, H>), dim3(a.nwg), dim3(NW * kWave), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((attn_stream_rescale<DK, NW, false, H>), dim3(a.nwg), dim3(NW * kWave),
+                       0, stream, a);
+}
+
 template <int DK>
-hipError_t launch_dk(const Bf16Args &base, int BH, bool short_path, bool out_f32,
+void launch_fix(Args16 a, int BH, bool out_f32, hipStream_t stream) {
+  constexpr int NW = kStreamFixWaves;
+  a.qblocks = (a.Lq + NW * kQW - 1) / (NW * kQW);
+  a.nwg = BH * a.qblocks;
+  if (out_f32)
+    hipLaunchKernelGGL((attn_stream_fix<DK, NW, true>), dim3(a.nwg), dim3(NW * kWave), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((attn_stream_fix<DK, NW, false>), dim3(a.nwg), dim3(NW * kWave), 0,
+                       stream, a);
+}
+
+// bf16: short-key kernel, else the fixed-reference kernel up to DK 64 and
+// the rescaling kernel above.  fp16 weights would overflow fp16's range
+// under a fixed reference, so fp16 streams through the rescaling kernel
+// (weights <= 2^8) at every head dim.
+template <int DK>
+hipError_t launch_dk(const Args16 &a, int BH, bool short_path, bool out_f32, bool half,
                      hipStream_t stream) {
-  Bf16Args a = base;
-  if (short_path) {
-    const int per_wg = kShortWaves * kQW * kShortTiles;
-    a.qblocks = (a.Lq + per_wg - 1) / per_wg;
-    a.nwg = BH * a.qblocks;
-    if (a.Lk <= 128) {
-      if (out_f32)
-        hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, 128, true>),
-                           dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
-      else
-        hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, 128, false>),
-                           dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
-    } else if constexpr (short_cap<DK>() > 128) {
-      if (out_f32)
-        hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, 256, true>),
-                           dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
-      else
-        hipLaunchKernelGGL((attn_short_bf16<DK, kShortWaves, kShortTiles, 256, false>),
-                           dim3(a.nwg), dim3(kShortWaves * kWave), 0, stream, a);
-    } else {
-      return hipErrorInvalidValue;  // the API checks Lk against the cap first
-    }
+  if (half) {
+    if (short_path) launch_short<DK, true>(a, BH, out_f32, stream);
+    else launch_rescale<DK, true>(a, BH, out_f32, stream);
+  } else if (short_path) {
+    launch_short<DK, false>(a, BH, out_f32, stream);
   } else if constexpr (DK <= kStreamFixMaxDk) {
-    constexpr int NW = kStreamFixWaves;
-    const int per_wg = NW * kQW;
-    a.qblocks = (a.Lq + per_wg - 1) / per_wg;
-    a.nwg = BH * a.qblocks;
-    if (out_f32)
-      hipLaunchKernelGGL((attn_stream_fix_bf16<DK, NW, true>), dim3(a.nwg), dim3(NW * kWave),
-                         0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_stream_fix_bf16<DK, NW, false>), dim3(a.nwg), dim3(NW * kWave),
-                         0, stream, a);
+    launch_fix<DK>(a, BH, out_f32, stream);
   } else {
-    const int per_wg = kStreamWaves * kQW;
-    a.qblocks = (a.Lq + per_wg - 1) / per_wg;
-    a.nwg = BH * a.qblocks;
-    if (out_f32)
-      hipLaunchKernelGGL((attn_stream_dma_bf16<DK, kStreamWaves, true>),
-                         dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_stream_dma_bf16<DK, kStreamWaves, false>),
-                         dim3(a.nwg), dim3(kStreamWaves * kWave), 0, stream, a);
+    launch_rescale<DK, false>(a, BH, out_f32, stream);
   }
   return hipGetLastError();
 }
@@ -1158,26 +1167,26 @@ int short_path_max_keys(int d) {
   return short_cap<16>();
 }
 
-hipError_t launch_bf16(const Bf16Args &a, int BH, bool short_path, bool out_f32,
-                       hipStream_t stream) {
+hipError_t launch_16(const Args16 &a, int BH, bool short_path, bool out_f32, bool half,
+                     hipStream_t stream) {
   const int dk = (a.d + 15) / 16 * 16;
   switch (dk) {
-    case 16: return launch_dk<16>(a, BH, short_path, out_f32, stream);
-    case 32: return launch_dk<32>(a, BH, short_path, out_f32, stream);
-    case 48: return launch_dk<48>(a, BH, short_path, out_f32, stream);
-    case 64: return launch_dk<64>(a, BH, short_path, out_f32, stream);
-    case 80: return launch_dk<80>(a, BH, short_path, out_f32, stream);
-    case 96: return launch_dk<96>(a, BH, short_path, out_f32, stream);
-    case 112: return launch_dk<112>(a, BH, short_path, out_f32, stream);
-    case 128: return launch_dk<128>(a, BH, short_path, out_f32, stream);
-    case 144: return launch_dk<144>(a, BH, short_path, out_f32, stream);
-    case 160: return launch_dk<160>(a, BH, short_path, out_f32, stream);
-    case 176: return launch_dk<176>(a, BH, short_path, out_f32, stream);
-    case 192: return launch_dk<192>(a, BH, short_path, out_f32, stream);
-    case 208: return launch_dk<208>(a, BH, short_path, out_f32, stream);
-    case 224: return launch_dk<224>(a, BH, short_path, out_f32, stream);
-    case 240: return launch_dk<240>(a, BH, short_path, out_f32, stream);
-    case 256: return launch_dk<256>(a, BH, short_path, out_f32, stream);
+    case 16: return launch_dk<16>(a, BH, short_path, out_f32, half, stream);
+    case 32: return launch_dk<32>(a, BH, short_path, out_f32, half, stream);
+    case 48: return launch_dk<48>(a, BH, short_path, out_f32, half, stream);
+    case 64: return launch_dk<64>(a, BH, short_path, out_f32, half, stream);
+    case 80: return launch_dk<80>(a, BH, short_path, out_f32, half, stream);
+    case 96: return launch_dk<96>(a, BH, short_path, out_f32, half, stream);
+    case 112: return launch_dk<112>(a, BH, short_path, out_f32, half, stream);
+    case 128: return launch_dk<128>(a, BH, short_path, out_f32, half, stream);
+    case 144: return launch_dk<144>(a, BH, short_path, out_f32, half, stream);
+    case 160: return launch_dk<160>(a, BH, short_path, out_f32, half, stream);
+    case 176: return launch_dk<176>(a, BH, short_path, out_f32, half, stream);
+    case 192: return launch_dk<192>(a, BH, short_path, out_f32, half, stream);
+    case 208: return launch_dk<208>(a, BH, short_path, out_f32, half, stream);
+    case 224: return launch_dk<224>(a, BH, short_path, out_f32, half, stream);
+    case 240: return launch_dk<240>(a, BH, short_path, out_f32, half, stream);
+    case 256: return launch_dk<256>(a, BH, short_path, out_f32, half, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,9 +12,10 @@ namespace sdattn {
 // head dimension d.
 int short_path_max_keys(int d);
 
-// bf16 kernels.  a.qblocks and a.nwg are filled in by the launcher.
-hipError_t launch_bf16(const Bf16Args &a, int BH, bool short_path, bool out_f32,
-                       hipStream_t stream);
+// 16-bit kernels (bf16, or fp16 when half).  a.qblocks and a.nwg are filled
+// in by the launcher.
+hipError_t launch_16(const Args16 &a, int BH, bool short_path, bool out_f32, bool half,
+                     hipStream_t stream);
 
 // fp32 kernel (any Lk).
 hipError_t launch_f32(const F32Args &a, int BH, hipStream_t stream);

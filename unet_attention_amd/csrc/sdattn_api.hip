@@ -55,11 +55,24 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 enum class Path { Auto, Short, Stream };
 
+bool known_dtype(int dtype) {
+  return dtype == SDATTN_DTYPE_F32 || dtype == SDATTN_DTYPE_BF16 ||
+         dtype == SDATTN_DTYPE_BF16_F32OUT || dtype == SDATTN_DTYPE_F16 ||
+         dtype == SDATTN_DTYPE_F16_F32OUT;
+}
+
+bool half_dtype(int dtype) {
+  return dtype == SDATTN_DTYPE_F16 || dtype == SDATTN_DTYPE_F16_F32OUT;
+}
+
+bool f32_out(int dtype) {
+  return dtype == SDATTN_DTYPE_F32 || dtype == SDATTN_DTYPE_BF16_F32OUT ||
+         dtype == SDATTN_DTYPE_F16_F32OUT;
+}
+
 int validate(const void *q, const void *k, const void *v, void *out, int B,
              int H, int Lq, int Lk, int d, float scale, int dtype) {
-  if (dtype != SDATTN_DTYPE_F32 && dtype != SDATTN_DTYPE_BF16 &&
-      dtype != SDATTN_DTYPE_BF16_F32OUT)
-    return SDATTN_ERR_INVALID_ARG;
+  if (!known_dtype(dtype)) return SDATTN_ERR_INVALID_ARG;
   if (!q || !k || !v || !out) return SDATTN_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || Lq < 1 || Lk < 1 || d < 1) return SDATTN_ERR_INVALID_ARG;
   if (!isfinite(scale)) return SDATTN_ERR_INVALID_ARG;
@@ -69,7 +82,7 @@ int validate(const void *q, const void *k, const void *v, void *out, int B,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return SDATTN_ERR_MISALIGNED;
   const int64_t ein = (dtype == SDATTN_DTYPE_F32) ? 4 : 2;
-  const int64_t eout = (dtype == SDATTN_DTYPE_BF16) ? 2 : 4;
+  const int64_t eout = f32_out(dtype) ? 4 : 2;
   const int64_t nout = nq * eout;
   if (overlaps(out, nout, q, nq * ein) || overlaps(out, nout, k, nk * ein) ||
       overlaps(out, nout, v, nk * ein))
@@ -100,7 +113,7 @@ int run(const void *q, const void *k, const void *v, void *out, int B, int H,
     a.scale = scale;
     err = sdattn::launch_f32(a, B * H, s);
   } else {
-    sdattn::Bf16Args a{};
+    sdattn::Args16 a{};
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
     a.v = static_cast<const uint16_t *>(v);
@@ -112,8 +125,7 @@ int run(const void *q, const void *k, const void *v, void *out, int B, int H,
     a.qsign = (scale < 0.f) ? 0x80008000u : 0u;
     const bool short_path =
         (path == Path::Short) || (path == Path::Auto && Lk <= cap);
-    err = sdattn::launch_bf16(a, B * H, short_path,
-                              dtype == SDATTN_DTYPE_BF16_F32OUT, s);
+    err = sdattn::launch_16(a, B * H, short_path, f32_out(dtype), half_dtype(dtype), s);
   }
   return (err == hipSuccess) ? SDATTN_OK : SDATTN_ERR_LAUNCH;
 }
@@ -142,9 +154,7 @@ int sdattn_stream_fwd(const void *q, const void *k, const void *v, void *out,
 }
 
 int sdattn_cross_max_ctx(int d, int dtype) {
-  if (dtype != SDATTN_DTYPE_F32 && dtype != SDATTN_DTYPE_BF16 &&
-      dtype != SDATTN_DTYPE_BF16_F32OUT)
-    return 0;
+  if (!known_dtype(dtype)) return 0;
   if (d < 8 || d > 256 || d % 8 != 0) return 0;
   return sdattn::short_path_max_keys(d);
 }
@@ -161,6 +171,6 @@ const char *sdattn_strerror(int status) {
   }
 }
 
-int sdattn_version(void) { return 10000; }
+int sdattn_version(void) { return 10100; }
 
 }  // extern "C"

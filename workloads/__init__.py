@@ -15,11 +15,12 @@ here and none are needed.
 Recipe (identical for every consumer):
   * rng = numpy.random.default_rng(seed); q, k, v are drawn in that order,
     each as float32 standard normals in C order of [B, H, L, d];
-  * bf16 workloads round each float32 to bf16 with round-to-nearest-even;
-    both sides then see exactly the rounded values;
+  * bf16 (fp16) workloads round each float32 to bf16 (fp16) with
+    round-to-nearest-even; both sides then see exactly the rounded values;
   * heavy-key workloads pick, per (b, h) in order, round(frac * Lk) key rows
     without replacement from the same generator (after v) and multiply those
-    rows by a power of two (exact in bf16), to stress running-max tracking.
+    rows by a power of two (exact in bf16 and fp16 at these magnitudes), to
+    stress running-max tracking.
 """
 from __future__ import annotations
 
@@ -88,6 +89,14 @@ WORKLOADS = {
     "5": Workload("5", "self", 8, 10, 16384, 16384, 64, "bf16", 5000,
                   heavy_frac=0.01, heavy_mult=8.0,
                   note="self-attention, 128x128 latent, 1% of keys x8"),
+    # fp16 storage of the 64x64-latent pair and of the heavy-key workload.
+    "2h": Workload("2h", "self", 2, 8, 4096, 4096, 40, "f16", 2100,
+                   note="self-attention, 64x64 latent, fp16"),
+    "3h": Workload("3h", "cross", 2, 8, 4096, 77, 40, "f16", 3100,
+                   note="cross-attention, 64x64 latent, 77-token context, fp16"),
+    "5h": Workload("5h", "self", 8, 10, 16384, 16384, 64, "f16", 5100,
+                   heavy_frac=0.01, heavy_mult=8.0,
+                   note="self-attention, 128x128 latent, 1% of keys x8, fp16"),
     # Longer text contexts than CLIP's 77 tokens (several concatenated prompt
     # chunks, or larger text encoders), 64x64 latent.
     "6a": Workload("6a", "cross", 2, 8, 4096, 256, 40, "bf16", 6001,
@@ -117,7 +126,7 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 @dataclass
 class Inputs:
     """Q, K, V as float32 values (exactly the stored values) and, for bf16
-    workloads, their bf16 bit patterns."""
+    and fp16 workloads, their 16-bit patterns."""
     w: Workload
     q: np.ndarray
     k: np.ndarray
@@ -140,6 +149,8 @@ def make_inputs(w: Workload) -> Inputs:
     if w.dtype == "bf16":
         qb, kb, vb = (round_to_bf16_bits(t) for t in (q, k, v))
         q, k, v = (bf16_bits_to_f32(t) for t in (qb, kb, vb))
+    elif w.dtype == "f16":
+        q, k, v = (t.astype(np.float16).astype(np.float32) for t in (q, k, v))
     if w.heavy_frac > 0.0:
         n = int(round(w.heavy_frac * w.Lk))
         heavy = np.empty((w.B, w.H, n), dtype=np.int64)
@@ -151,6 +162,10 @@ def make_inputs(w: Workload) -> Inputs:
         # Re-derive the bit patterns after the (exact) power-of-two scaling.
         qb, kb, vb = (round_to_bf16_bits(t) for t in (q, k, v))
         assert np.array_equal(bf16_bits_to_f32(kb), k)
+        return Inputs(w, q, k, v, qb, kb, vb, heavy)
+    if w.dtype == "f16":
+        qb, kb, vb = (t.astype(np.float16).view(np.uint16) for t in (q, k, v))
+        assert np.array_equal(kb.view(np.float16).astype(np.float32), k)
         return Inputs(w, q, k, v, qb, kb, vb, heavy)
     return Inputs(w, q, k, v, heavy_rows=heavy)
 
