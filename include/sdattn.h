@@ -99,6 +99,20 @@ int sdattn_stream_fwd(const void *q, const void *k, const void *v, void *out,
                       int B, int H, int Lq, int Lk, int d, float scale,
                       int dtype, void *stream);
 
+/* The same attention on token-major operands, as the page's section 3.2
+ * has them: activations [B, HW, C] with C = H*d and the head split implicit.
+ * q is [B, Lq, ldq], k and v are [B, Lk, ldkv], out is [B, Lq, ldo]
+ * (row-major; element (b, i, h*d + c) is head h, column c of token i).  A
+ * row stride larger than H*d lets q, k and v be column slices of one fused
+ * projection, e.g. [B, L, 3C] with k = q + C and v = q + 2C, ld = 3C.
+ * Requires every ld >= H*d and ld % 8 == 0 (else SDATTN_ERR_INVALID_ARG);
+ * the out rows must not overlap the inputs' spans.  Dispatch, dtypes and
+ * results are those of sdattn_fwd on the same values in [B, H, L, d]
+ * layout (bit-identical). */
+int sdattn_fwd_strided(const void *q, const void *k, const void *v, void *out,
+                       int B, int H, int Lq, int Lk, int d, int ldq, int ldkv,
+                       int ldo, float scale, int dtype, void *stream);
+
 /* Largest context length the short-key path accepts for this head dim and
  * dtype; 0 if (d, dtype) is unsupported. */
 int sdattn_cross_max_ctx(int d, int dtype);
@@ -106,7 +120,8 @@ int sdattn_cross_max_ctx(int d, int dtype);
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *sdattn_strerror(int status);
 
-/* ABI version: major * 10000 + minor * 100 + patch. */
+/* ABI version: major * 10000 + minor * 100 + patch (1.2: fp16 dtypes and
+ * sdattn_fwd_strided). */
 int sdattn_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert sd.sdattn_version() == 10100
+    assert sd.sdattn_version() == 10200
     seen = set()
     for code in range(6):
         msg = sd.sdattn_strerror(code)
@@ -133,3 +133,44 @@ def test_torch_wrapper_checks_shapes(lib):
         sd.fwd(q, q, q)  # CPU tensors are refused before any call
     with pytest.raises(ValueError):
         sd.fwd(q.to(torch.float16), q, q)
+
+
+def call_strided(**kw):
+    args = dict(q=Q, k=K, v=V, out=O, B=2, H=8, Lq=64, Lk=77, d=40, ldq=320, ldkv=320,
+                ldo=320, scale=1 / math.sqrt(40), dtype=sd.SDATTN_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return sd.sdattn_fwd_strided(*(args[n] for n in (
+        "q", "k", "v", "out", "B", "H", "Lq", "Lk", "d", "ldq", "ldkv", "ldo", "scale",
+        "dtype", "stream")))
+
+
+BAD_STRIDED = [
+    ("ldq_small", dict(ldq=312), sd.SDATTN_ERR_INVALID_ARG),     # < H*d
+    ("ldkv_small", dict(ldkv=8), sd.SDATTN_ERR_INVALID_ARG),
+    ("ldo_small", dict(ldo=40), sd.SDATTN_ERR_INVALID_ARG),
+    ("ldq_unaligned", dict(ldq=324), sd.SDATTN_ERR_INVALID_ARG),  # rows not 16-byte aligned
+    ("ldo_zero", dict(ldo=0), sd.SDATTN_ERR_INVALID_ARG),
+    ("ldkv_neg", dict(ldkv=-320), sd.SDATTN_ERR_INVALID_ARG),
+    ("null_v", dict(v=None), sd.SDATTN_ERR_INVALID_ARG),
+    ("dtype", dict(dtype=5), sd.SDATTN_ERR_INVALID_ARG),
+    ("d_odd", dict(d=41, ldq=328, ldkv=328, ldo=328), sd.SDATTN_ERR_UNSUPPORTED),
+    ("misaligned_k", dict(k=K + 8), sd.SDATTN_ERR_MISALIGNED),
+    # out's rows span B*Lq*320 elements: starting inside q's span overlaps it
+    ("out_overlaps_q", dict(out=Q + 2 * 320), sd.SDATTN_ERR_INVALID_ARG),
+    ("too_big", dict(Lq=1 << 22, ldq=1024, ldo=1024), sd.SDATTN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("case", BAD_STRIDED, ids=[b[0] for b in BAD_STRIDED])
+def test_strided_invalid_arguments(lib, case):
+    _, kw, want = case
+    assert call_strided(**kw) == want
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3, 4])
+def test_strided_valid_call_without_gpu_reports_device(lib, dtype):
+    if _gpu_present():
+        pytest.skip("a GPU is present; fake pointers must not reach a launch")
+    # fused projection layout: k and v are column slices of q's rows
+    assert call_strided(k=Q + 2 * 320, v=Q + 4 * 320, ldq=960, ldkv=960, Lk=64,
+                        dtype=dtype) == sd.SDATTN_ERR_DEVICE

@@ -355,3 +355,72 @@ def test_errors_on_device(dev):
     with pytest.raises(sd.SdattnError):
         sd.cross_fwd(q, torch.zeros(1, 1, cap + 1, 40, dtype=torch.bfloat16, device=dev),
                      torch.zeros(1, 1, cap + 1, 40, dtype=torch.bfloat16, device=dev))
+
+
+# ---------------------------------------------------------------------------
+# token-major operands (sdattn_fwd_strided)
+
+
+def _to_tokens(a):
+    """[B, H, L, d] -> [B, L, H*d] (numpy)."""
+    B, H, L, d = a.shape
+    return np.ascontiguousarray(a.transpose(0, 2, 1, 3).reshape(B, L, H * d))
+
+
+STRIDED_CASES = [  # (dtype, H, Lq, Lk, d): short-key, fixed-reference, rescaling, fp32
+    ("bf16", 2, 129, 77, 40), ("bf16", 3, 300, 300, 64), ("bf16", 2, 100, 333, 80),
+    ("f16", 2, 65, 200, 40), ("f32", 2, 33, 77, 40),
+]
+
+
+@pytest.mark.parametrize("dtype,H,Lq,Lk,d", STRIDED_CASES)
+def test_token_major_matches_head_major(dev, dtype, H, Lq, Lk, d):
+    """Packed [B, L, C] operands give the oracle's result and exactly the
+    head-major entry's output; also with an output of row stride 2C whose
+    other columns must stay untouched."""
+    import torch
+    import unet_attention_amd as sd
+    B = 2
+    w = Workload("tok", "self", B, H, Lq, Lk, d, dtype, 11000 + Lq + Lk + d)
+    x = make_inputs(w)
+    want = oracle.attn(x.q, x.k, x.v, w.scale)
+    q, k, v = to_device(x)
+    odt = torch.float32
+    ref = sd.fwd(q, k, v, scale=w.scale, out_dtype=odt)
+    qt, kt, vt = (t.permute(0, 2, 1, 3).reshape(B, t.shape[2], H * d).contiguous()
+                  for t in (q, k, v))
+    say(f"token-major {dtype} H={H} Lq={Lq} Lk={Lk} d={d}")
+    got = sd.fwd_tokens(qt, kt, vt, H, scale=w.scale, out_dtype=odt)
+    torch.cuda.synchronize()
+    got_hm = got.view(B, Lq, H, d).permute(0, 2, 1, 3).cpu().numpy().astype(np.float64)
+    gate = assert_f32_gate if dtype == "f32" else assert_bf16_gate
+    gate(got_hm, want, f"token-major {dtype}")
+    assert np.array_equal(got_hm, ref.cpu().numpy().astype(np.float64)), \
+        "token-major result differs from the head-major entry"
+    wide = torch.full((B, Lq, 2 * H * d), 7.0, dtype=odt, device=dev)
+    sd.fwd_tokens(qt, kt, vt, H, out=wide[:, :, :H * d], scale=w.scale, out_dtype=odt)
+    torch.cuda.synchronize()
+    assert torch.equal(wide[:, :, :H * d], got), "strided output differs"
+    assert bool((wide[:, :, H * d:] == 7.0).all()), "columns outside the output were written"
+
+
+@pytest.mark.parametrize("dtype,Lk", [("bf16", 77), ("bf16", 256), ("f16", 256)])
+def test_fused_qkv_projection_slices(dev, dtype, Lk):
+    """q, k, v as column slices of one [B, L, 3C] projection (row stride 3C)."""
+    import torch
+    import unet_attention_amd as sd
+    B, H, d = 2, 4, 64
+    L = Lk
+    w = Workload("qkv", "self", B, H, L, L, d, dtype, 12000 + Lk)
+    x = make_inputs(w)
+    want = oracle.attn(x.q, x.k, x.v, w.scale)
+    q, k, v = to_device(x)
+    C = H * d
+    qkv = torch.cat([t.permute(0, 2, 1, 3).reshape(B, L, C) for t in (q, k, v)], dim=2)
+    qs, ks, vs = qkv[:, :, :C], qkv[:, :, C:2 * C], qkv[:, :, 2 * C:]
+    assert qs.stride(1) == 3 * C
+    say(f"fused qkv {dtype} L={L}")
+    got = sd.fwd_tokens(qs, ks, vs, H, scale=w.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got_hm = got.view(B, L, H, d).permute(0, 2, 1, 3).cpu().numpy().astype(np.float64)
+    assert_bf16_gate(got_hm, want, f"fused qkv {dtype} L={L}")

@@ -40,6 +40,8 @@ EXPORTS = {
     "sdattn_fwd": (_I, _ATTN_ARGS),
     "sdattn_cross_fwd": (_I, _ATTN_ARGS),
     "sdattn_stream_fwd": (_I, _ATTN_ARGS),
+    "sdattn_fwd_strided": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I,
+                                ctypes.c_float, _I, _VP]),
     "sdattn_cross_max_ctx": (_I, [_I, _I]),
     "sdattn_strerror": (ctypes.c_char_p, [_I]),
     "sdattn_version": (_I, []),
@@ -88,6 +90,11 @@ def sdattn_stream_fwd(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, stream):
     return load().sdattn_stream_fwd(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, stream)
 
 
+def sdattn_fwd_strided(q, k, v, out, B, H, Lq, Lk, d, ldq, ldkv, ldo, scale, dtype, stream):
+    return load().sdattn_fwd_strided(q, k, v, out, B, H, Lq, Lk, d, ldq, ldkv, ldo,
+                                     scale, dtype, stream)
+
+
 def sdattn_cross_max_ctx(d, dtype):
     return load().sdattn_cross_max_ctx(d, dtype)
 
@@ -107,31 +114,28 @@ _ENTRIES = {"auto": "sdattn_fwd", "cross": "sdattn_cross_fwd",
             "stream": "sdattn_stream_fwd"}
 
 
-def _call(entry, q, k, v, out=None, scale=None, out_dtype=None, stream=None):
+def _dtype_code(in_dtype, out_dtype):
+    """(sdattn dtype code, output torch dtype) for an input/output pair."""
     import torch
-    if q.dtype == torch.float32:
-        dtype_code = SDATTN_DTYPE_F32
-        odt = torch.float32
+    if in_dtype == torch.float32:
         if out_dtype not in (None, torch.float32):
             raise ValueError("fp32 inputs produce fp32 output")
-    elif q.dtype == torch.bfloat16:
-        odt = out_dtype or torch.bfloat16
-        if odt == torch.bfloat16:
-            dtype_code = SDATTN_DTYPE_BF16
-        elif odt == torch.float32:
-            dtype_code = SDATTN_DTYPE_BF16_F32OUT
-        else:
-            raise ValueError(f"unsupported output dtype {odt}")
-    elif q.dtype == torch.float16:
-        odt = out_dtype or torch.float16
-        if odt == torch.float16:
-            dtype_code = SDATTN_DTYPE_F16
-        elif odt == torch.float32:
-            dtype_code = SDATTN_DTYPE_F16_F32OUT
-        else:
-            raise ValueError(f"unsupported output dtype {odt}")
-    else:
-        raise ValueError(f"unsupported input dtype {q.dtype}")
+        return SDATTN_DTYPE_F32, torch.float32
+    codes = {torch.bfloat16: (SDATTN_DTYPE_BF16, SDATTN_DTYPE_BF16_F32OUT),
+             torch.float16: (SDATTN_DTYPE_F16, SDATTN_DTYPE_F16_F32OUT)}
+    if in_dtype not in codes:
+        raise ValueError(f"unsupported input dtype {in_dtype}")
+    odt = out_dtype or in_dtype
+    if odt == in_dtype:
+        return codes[in_dtype][0], odt
+    if odt == torch.float32:
+        return codes[in_dtype][1], odt
+    raise ValueError(f"unsupported output dtype {odt}")
+
+
+def _call(entry, q, k, v, out=None, scale=None, out_dtype=None, stream=None):
+    import torch
+    dtype_code, odt = _dtype_code(q.dtype, out_dtype)
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != q.dtype:
             raise ValueError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
@@ -170,3 +174,46 @@ def cross_fwd(q, ctx_k, ctx_v, out=None, scale=None, out_dtype=None, stream=None
 def stream_fwd(q, k, v, out=None, scale=None, out_dtype=None, stream=None):
     """Always the streaming (online-softmax) kernel, via sdattn_stream_fwd."""
     return _call("stream", q, k, v, out, scale, out_dtype, stream)
+
+
+def fwd_tokens(q, k, v, heads, out=None, scale=None, out_dtype=None, stream=None):
+    """Attention on token-major operands via sdattn_fwd_strided.
+
+    q is [B, Lq, C] and k, v are [B, Lk, C] with C = heads * d, each with
+    unit column stride and any row stride (so column slices of a fused
+    [B, L, 3C] projection work directly); head h is columns [h*d, (h+1)*d).
+    Returns (or fills) out as [B, Lq, C].
+    """
+    import torch
+    dtype_code, odt = _dtype_code(q.dtype, out_dtype)
+    if k.stride() != v.stride():
+        raise ValueError("k and v must have the same strides")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+        if not t.is_cuda or t.dim() != 3 or t.stride(2) != 1 or \
+                t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError(f"{name} must be a [B, L, C] device tensor with unit column "
+                             "stride and batch stride L * row stride")
+    B, Lq, C = q.shape
+    Lk = k.shape[1]
+    if C % heads:
+        raise ValueError(f"C = {C} is not a multiple of heads = {heads}")
+    d = C // heads
+    if tuple(k.shape) != (B, Lk, C) or tuple(v.shape) != (B, Lk, C):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out is None:
+        out = torch.empty((B, Lq, C), dtype=odt, device=q.device)
+    elif out.dtype != odt or tuple(out.shape) != (B, Lq, C) or out.stride(2) != 1 or \
+            out.stride(0) != Lq * out.stride(1):
+        raise ValueError("out must be a [B, Lq, C] tensor of the output dtype")
+    if scale is None:
+        scale = float(1.0 / math.sqrt(d))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = load().sdattn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   B, heads, Lq, Lk, d, q.stride(1), k.stride(1),
+                                   out.stride(1), scale, dtype_code, stream)
+    if rc != SDATTN_OK:
+        raise SdattnError(rc, "sdattn_fwd_strided")
+    return out

@@ -22,13 +22,34 @@ constexpr float kLog2e = 1.4426950408889634f;
 // exact arithmetic because l and O always share the same stale m.
 constexpr float kRescaleSlack = 8.0f;
 
-// Arguments common to the 16-bit (bf16 or fp16) kernels.  Pointers are
-// [B, H, L, d] contiguous; q/k/v hold 16-bit element bit patterns.
+// Placement of one [B, H, L, d] operand: element (b, h, i, c) lives at
+// b*sb + h*sh + i*sl + c elements from the base pointer.  Contiguous
+// [B, H, L, d]: sb = H*L*d, sh = L*d, sl = d.  Token-major [B, L, ld] with
+// head h in columns [h*d, h*d + d): sb = L*ld, sh = d, sl = ld.
+struct Layout {
+  long long sb;
+  int sh, sl;
+  __host__ __device__ size_t head(int bh, int H) const {
+    const int b = bh / H;
+    return (size_t)b * (size_t)sb + (size_t)(bh - b * H) * (size_t)sh;
+  }
+};
+
+// Bytes from a head's first element to the end of its last row: rows at or
+// past L start beyond this, so range-checked loads read them as zero.
+__device__ __forceinline__ uint32_t head_span_bytes(int L, int sl, int d, int esz) {
+  return (uint32_t)((L - 1) * sl + d) * (uint32_t)esz;
+}
+
+// Arguments common to the 16-bit (bf16 or fp16) kernels; q/k/v hold 16-bit
+// element bit patterns, v is placed like k.
 struct Args16 {
   const uint16_t *q;
   const uint16_t *k;
   const uint16_t *v;
   void *out;
+  int H;
+  Layout lq, lk, lo;
   int Lq, Lk, d;
   int qblocks;     // workgroups per (b, h)
   int nwg;         // total workgroups
@@ -41,6 +62,8 @@ struct F32Args {
   const float *k;
   const float *v;
   float *out;
+  int H;
+  Layout lq, lk, lo;
   int Lq, Lk, d;
   int qblocks;
   float scale;

@@ -36,13 +36,14 @@ __global__ __launch_bounds__(kWave) void attn_f32_kernel(F32Args a) {
   const int bh = blockIdx.x / a.qblocks;
   const int q0 = (blockIdx.x - bh * a.qblocks) * kQB;
   const int d = a.d, Lq = a.Lq, Lk = a.Lk;
-  const float *qg = a.q + (size_t)bh * Lq * d;
-  const float *kg = a.k + (size_t)bh * Lk * d;
-  const float *vg = a.v + (size_t)bh * Lk * d;
+  const int slq = a.lq.sl, slk = a.lk.sl, slo = a.lo.sl;
+  const float *qg = a.q + a.lq.head(bh, a.H);
+  const float *kg = a.k + a.lk.head(bh, a.H);
+  const float *vg = a.v + a.lk.head(bh, a.H);
 
   for (int idx = lane; idx < kQB * d; idx += kWave) {
     const int r = idx / d, cc = idx - r * d;
-    qs[idx] = (q0 + r < Lq) ? qg[(size_t)(q0 + r) * d + cc] : 0.f;
+    qs[idx] = (q0 + r < Lq) ? qg[(size_t)(q0 + r) * slq + cc] : 0.f;
   }
   __syncthreads();
 
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(kWave) void attn_f32_kernel(F32Args a) {
     float s[kQB];
 #pragma unroll
     for (int r = 0; r < kQB; ++r) s[r] = 0.f;
-    const float *kr = kg + (size_t)(valid ? j : 0) * d;
+    const float *kr = kg + (size_t)(valid ? j : 0) * slk;
     for (int cc = 0; cc < d; cc += 4) {
       f32x4 kv = {0.f, 0.f, 0.f, 0.f};
       if (valid) kv = *reinterpret_cast<const f32x4 *>(kr + cc);
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kWave) void attn_f32_kernel(F32Args a) {
     __syncthreads();
     const int nj = min(kWave, Lk - j0);
     for (int jj = 0; jj < nj; ++jj) {
-      const float *vr = vg + (size_t)(j0 + jj) * d;
+      const float *vr = vg + (size_t)(j0 + jj) * slk;
       float vv[DU];
 #pragma unroll
       for (int u = 0; u < DU; ++u) {
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kWave) void attn_f32_kernel(F32Args a) {
     __syncthreads();
   }
 
-  float *og = a.out + (size_t)bh * Lq * d;
+  float *og = a.out + a.lo.head(bh, a.H);
 #pragma unroll
   for (int r = 0; r < kQB; ++r) {
     if (q0 + r >= Lq) continue;
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(kWave) void attn_f32_kernel(F32Args a) {
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
       const int col = lane + kWave * u;
-      if (col < d) og[(size_t)(q0 + r) * d + col] = o[r][u] * inv;
+      if (col < d) og[(size_t)(q0 + r) * slo + col] = o[r][u] * inv;
     }
   }
 }

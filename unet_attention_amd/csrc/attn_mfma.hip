@@ -77,13 +77,13 @@ constexpr int waves_per_simd() { return DK <= 112 ? 2 : 1; }
 // columns dk*16 + 8*(l/32) .. +7; rows past Lq and columns past d are zero.
 template <int DK>
 __device__ __forceinline__ void load_q(bf16x8 (&qf)[DK / 16], rsrc_t qr, int q0,
-                                       int d, uint32_t qsign, int lane) {
+                                       int d, int sl, uint32_t qsign, int lane) {
   const int qi = q0 + (lane & 31);
   const int cb = 8 * (lane >> 5);
 #pragma unroll
   for (int dk = 0; dk < DK / 16; ++dk) {
     const int c0 = dk * 16 + cb;
-    u32x4 x = bload16(qr, (uint32_t)(qi * d + c0) * 2u);
+    u32x4 x = bload16(qr, (uint32_t)(qi * sl + c0) * 2u);
     if (c0 >= d) x = u32x4{0u, 0u, 0u, 0u};
     x ^= qsign;
     qf[dk] = as_bf16x8(x);
@@ -170,7 +170,7 @@ __device__ __forceinline__ float max16(const f32x16 &s, float m) {
 template <int DK, bool OUT_F32, bool H = false>
 __device__ __forceinline__ void store_out_l(const f32x16 (&o)[Shape<DK>::MT], float l,
                                             void *outp, size_t obase, int q0, int Lq,
-                                            int d, int lane) {
+                                            int d, int sl, int lane) {
   using S = Shape<DK>;
   const float inv = 1.0f / l;
   const int qi = q0 + (lane & 31);
@@ -184,7 +184,7 @@ __device__ __forceinline__ void store_out_l(const f32x16 (&o)[Shape<DK>::MT], fl
       if (c0 < d) {
         const float x0 = o[mt][4 * g4 + 0] * inv, x1 = o[mt][4 * g4 + 1] * inv;
         const float x2 = o[mt][4 * g4 + 2] * inv, x3 = o[mt][4 * g4 + 3] * inv;
-        const size_t off = obase + (size_t)qi * d + c0;
+        const size_t off = obase + (size_t)qi * sl + c0;
         if constexpr (OUT_F32) {
           f32x4 x = {x0, x1, x2, x3};
           *reinterpret_cast<f32x4 *>(static_cast<float *>(outp) + off) = x;
@@ -201,7 +201,7 @@ __device__ __forceinline__ void store_out_l(const f32x16 (&o)[Shape<DK>::MT], fl
 template <int DK, bool OUT_F32, bool H = false>
 __device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::MT],
                                           float lsum, void *outp, size_t obase,
-                                          int q0, int Lq, int d, int lane) {
+                                          int q0, int Lq, int d, int sl, int lane) {
   using S = Shape<DK>;
   float l;
   if constexpr (S::kOnes) {
@@ -216,7 +216,7 @@ __device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::MT],
   } else {
     l = sum_halves(lsum);
   }
-  store_out_l<DK, OUT_F32, H>(o, l, outp, obase, q0, Lq, d, lane);
+  store_out_l<DK, OUT_F32, H>(o, l, outp, obase, q0, Lq, d, sl, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -350,9 +350,11 @@ void attn_stream_rescale(Args16 a) {
   const int q0 = (wg - bh * a.qblocks) * (NW * kQW) + wave * kQW;
   const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
   const float c = a.c;
-  const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
-  const u32x4 kw = rsrc_words(a.k + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
-  const u32x4 vw = rsrc_words(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  const int slq = a.lq.sl, slk = a.lk.sl;
+  const uint32_t kvbytes = head_span_bytes(Lk, slk, d, 2);
+  const rsrc_t qr = make_rsrc(a.q + a.lq.head(bh, a.H), head_span_bytes(Lq, slq, d, 2));
+  const u32x4 kw = rsrc_words(a.k + a.lk.head(bh, a.H), kvbytes);
+  const u32x4 vw = rsrc_words(a.v + a.lk.head(bh, a.H), kvbytes);
   const int ntiles = (Lk + BN - 1) / BN;
   const bool ragged = (Lk % BN) != 0;
 
@@ -370,7 +372,7 @@ void attn_stream_rescale(Args16 a) {
     const int cr = isk[r] ? P::KCR : P::VCR;
     const int row = cpos / cr, col = cpos - row * cr;
     act[r] = (i < P::NI) && row < BN && col < d8;
-    goff[r] = (uint32_t)(row * d + col * 8) * 2u;
+    goff[r] = (uint32_t)(row * slk + col * 8) * 2u;
     loff[r] = blk * 512;
   }
   // Transfers this wave really issues per tile (one with no active lane is
@@ -380,7 +382,7 @@ void attn_stream_rescale(Args16 a) {
   for (int r = 0; r < P::NIW; ++r)
     if (wave + NW * r < P::NI && __any(act[r])) ++my_count;
   auto issue = [&](int tt, int b) {
-    const uint32_t toff = (uint32_t)(tt * BN * d) * 2u;
+    const uint32_t toff = (uint32_t)(tt * BN * slk) * 2u;
 #pragma unroll
     for (int r = 0; r < P::NIW; ++r) {
       if (wave + NW * r < P::NI) {
@@ -394,7 +396,7 @@ void attn_stream_rescale(Args16 a) {
   };
 
   bf16x8 qf[DK / 16];
-  load_q<DK>(qf, qr, q0, d, a.qsign, lane);
+  load_q<DK>(qf, qr, q0, d, slq, a.qsign, lane);
   issue(0, 0);
   if (ntiles > 1) issue(1, 1);
 
@@ -519,7 +521,7 @@ void attn_stream_rescale(Args16 a) {
     step(B0{}, Ragged{}, t);
   }
 
-  store_out<DK, OUT_F32, H>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
+  store_out<DK, OUT_F32, H>(o, lsum, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -544,7 +546,8 @@ void attn_stream_rescale(Args16 a) {
 template <int DK>
 __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
                                             const bf16x8 (&qf)[DK / 16], rsrc_t kr,
-                                            rsrc_t vr, int Lk, int d, float c, int lane) {
+                                            rsrc_t vr, int Lk, int d, int sl, float c,
+                                            int lane) {
   using S = Shape<DK>;
 #pragma unroll
   for (int mt = 0; mt < S::MT; ++mt) o[mt] = f32x16{};
@@ -555,7 +558,7 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
 #pragma unroll
     for (int dk = 0; dk < DK / 16; ++dk) {
       const int c0 = dk * 16 + 8 * h;
-      u32x4 x = bload16(kr, (uint32_t)((key0 + r32) * d + c0) * 2u);
+      u32x4 x = bload16(kr, (uint32_t)((key0 + r32) * sl + c0) * 2u);
       if (c0 >= d) x = u32x4{0u, 0u, 0u, 0u};
       sv = mfma32x32x16(as_bf16x8(x), qf[dk], sv);
     }
@@ -602,7 +605,7 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
             const int j = 2 * j2 + e2;
             const int key = key0 + 16 * kk + 8 * (j >> 2) + 4 * h + (j & 3);
             e[e2] = col < d ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-                                  vr, (uint32_t)(key * d + col) * 2u, 0, 0)
+                                  vr, (uint32_t)(key * sl + col) * 2u, 0, 0)
                             : 0u;
           }
           w[j2] = e[0] | (e[1] << 16);
@@ -641,10 +644,11 @@ void attn_stream_fix(Args16 a) {
   const int q0 = (wg - bh * a.qblocks) * (NW * kQW) + wave * kQW;
   const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
   const float c = a.c;
-  const uint16_t *const kbase = a.k + (size_t)bh * Lk * d;
-  const uint16_t *const vbase = a.v + (size_t)bh * Lk * d;
-  const uint32_t kvbytes = (uint32_t)(Lk * d) * 2u;
-  const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
+  const int slq = a.lq.sl, slk = a.lk.sl;
+  const uint16_t *const kbase = a.k + a.lk.head(bh, a.H);
+  const uint16_t *const vbase = a.v + a.lk.head(bh, a.H);
+  const uint32_t kvbytes = head_span_bytes(Lk, slk, d, 2);
+  const rsrc_t qr = make_rsrc(a.q + a.lq.head(bh, a.H), head_span_bytes(Lq, slq, d, 2));
   const rsrc_t kr = make_rsrc(kbase, kvbytes);
   const rsrc_t vr = make_rsrc(vbase, kvbytes);
   const u32x4 kw = rsrc_words(kbase, kvbytes), vw = rsrc_words(vbase, kvbytes);
@@ -667,7 +671,7 @@ void attn_stream_fix(Args16 a) {
     const int cr = isk[r] ? P::KCR : P::VCR;
     const int row = cpos / cr, col = cpos - row * cr;
     act[r] = (i < P::NI) && row < BN && col < d8;
-    goff[r] = (uint32_t)(row * d + col * 8) * 2u;
+    goff[r] = (uint32_t)(row * slk + col * 8) * 2u;
     loff[r] = (uint32_t)blk * 1024u;
   }
   // Transfers this wave issues per K tile and per V tile (an instruction
@@ -680,7 +684,7 @@ void attn_stream_fix(Args16 a) {
     }
   const uint32_t ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
   auto issue_k = [&](int tt, int b) {
-    const uint32_t toff = (uint32_t)(tt * BN * d) * 2u;
+    const uint32_t toff = (uint32_t)(tt * BN * slk) * 2u;
     const uint32_t dst = ks_lds + (uint32_t)(b * P::KBUF) * 2u;
 #pragma unroll
     for (int r = 0; r < P::NIW; ++r)
@@ -688,7 +692,7 @@ void attn_stream_fix(Args16 a) {
         if (act[r]) dma16_raw(kw, toff + goff[r], dst + loff[r]);
   };
   auto issue_v = [&](int tt, int b) {
-    const uint32_t toff = (uint32_t)(tt * BN * d) * 2u;
+    const uint32_t toff = (uint32_t)(tt * BN * slk) * 2u;
     const uint32_t dst = vs_lds + (uint32_t)(b * P::VBUF) * 2u;
 #pragma unroll
     for (int r = 0; r < P::NIW; ++r)
@@ -703,7 +707,7 @@ void attn_stream_fix(Args16 a) {
   };
 
   bf16x8 qf[DK / 16];
-  load_q<DK>(qf, qr, q0, d, a.qsign, lane);
+  load_q<DK>(qf, qr, q0, d, slq, a.qsign, lane);
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
     if (u < n) issue_k(u, u);
@@ -885,9 +889,9 @@ void attn_stream_fix(Args16 a) {
   for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) ok = ok && __builtin_isfinite(o[mt][i]);
-  if (__any(!ok)) l = rows_exact<DK>(o, qf, kr, vr, Lk, d, c, lane);
+  if (__any(!ok)) l = rows_exact<DK>(o, qf, kr, vr, Lk, d, slk, c, lane);
 
-  store_out_l<DK, OUT_F32>(o, l, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
+  store_out_l<DK, OUT_F32>(o, l, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -899,7 +903,7 @@ void attn_stream_fix(Args16 a) {
 template <int DK, bool OUT_F32, bool H = false>
 __device__ __forceinline__ void store_out_staged(const f32x16 (&o)[Shape<DK>::MT],
                                                  float lsum, void *outp, size_t obase,
-                                                 int q0, int Lq, int d, int lane,
+                                                 int q0, int Lq, int d, int sl, int lane,
                                                  uint8_t *stage) {
   using S = Shape<DK>;
   constexpr int ELT = OUT_F32 ? 4 : 2;
@@ -937,11 +941,14 @@ __device__ __forceinline__ void store_out_staged(const f32x16 (&o)[Shape<DK>::MT
   // writes above.
   const int rows = min(kQW, Lq - q0);
   if (rows <= 0) return;
-  const int nchunks = rows * d * ELT / 16;
-  uint8_t *gdst = static_cast<uint8_t *>(outp) + (obase + (size_t)q0 * d) * ELT;
-  for (int ch = lane; ch < nchunks; ch += kWave)
-    *reinterpret_cast<u32x4 *>(gdst + (size_t)ch * 16) =
+  const int cpr = d * ELT / 16;  // 16-byte chunks per row (d % 8 == 0)
+  const int nchunks = rows * cpr;
+  uint8_t *gdst = static_cast<uint8_t *>(outp) + (obase + (size_t)q0 * sl) * ELT;
+  for (int ch = lane; ch < nchunks; ch += kWave) {
+    const int r = ch / cpr, cc = ch - r * cpr;
+    *reinterpret_cast<u32x4 *>(gdst + ((size_t)r * sl * ELT + cc * 16)) =
         *reinterpret_cast<const u32x4 *>(stage + ch * 16);
+  }
 }
 
 template <int DK, int NW, int QPW, int KMAX, bool OUT_F32, bool H>
@@ -968,9 +975,11 @@ void attn_short(Args16 a) {
   const int qbase = (wg - bh * a.qblocks) * (NW * kQW * QPW);
   const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
   const float c = a.c;
-  const rsrc_t qr = make_rsrc(a.q + (size_t)bh * Lq * d, (uint32_t)(Lq * d) * 2u);
-  const rsrc_t kr = make_rsrc(a.k + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
-  const rsrc_t vr = make_rsrc(a.v + (size_t)bh * Lk * d, (uint32_t)(Lk * d) * 2u);
+  const int slq = a.lq.sl, slk = a.lk.sl;
+  const uint32_t kvbytes = head_span_bytes(Lk, slk, d, 2);
+  const rsrc_t qr = make_rsrc(a.q + a.lq.head(bh, a.H), head_span_bytes(Lq, slq, d, 2));
+  const rsrc_t kr = make_rsrc(a.k + a.lk.head(bh, a.H), kvbytes);
+  const rsrc_t vr = make_rsrc(a.v + a.lk.head(bh, a.H), kvbytes);
   const int nkt = (Lk + 31) >> 5;
   const int keys = nkt * 32;
   const int ngroups = keys / 4;
@@ -978,14 +987,14 @@ void attn_short(Args16 a) {
   // Issue every HBM load first (this wave's first Q tile, all of K, all of
   // V), so their latencies overlap; only then write LDS.
   bf16x8 qf[DK / 16];
-  load_q<DK>(qf, qr, qbase + wave * kQW, d, a.qsign, lane);
+  load_q<DK>(qf, qr, qbase + wave * kQW, d, slq, a.qsign, lane);
   u32x4 kreg[KCH];
   u32x4 vreg[VCH][4];
 #pragma unroll
   for (int t = 0; t < KCH; ++t) {
     const int idx = tid + t * NT;
     const int row = idx / S::DK8, ch = idx - row * S::DK8;
-    if (row < keys && ch < d8) kreg[t] = bload16(kr, (uint32_t)(row * d + ch * 8) * 2u);
+    if (row < keys && ch < d8) kreg[t] = bload16(kr, (uint32_t)(row * slk + ch * 8) * 2u);
   }
 #pragma unroll
   for (int t = 0; t < VCH; ++t) {
@@ -994,7 +1003,7 @@ void attn_short(Args16 a) {
     if (g < ngroups && ch < d8) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vreg[t][r] = bload16(vr, (uint32_t)((4 * g + r) * d + ch * 8) * 2u);
+        vreg[t][r] = bload16(vr, (uint32_t)((4 * g + r) * slk + ch * 8) * 2u);
     }
   }
 
@@ -1021,7 +1030,7 @@ void attn_short(Args16 a) {
   for (int t = 0; t < QPW; ++t) {
     const int q0 = qbase + (t * NW + wave) * kQW;
     bf16x8 qn[DK / 16];
-    if (t + 1 < QPW) load_q<DK>(qn, qr, q0 + NW * kQW, d, a.qsign, lane);
+    if (t + 1 < QPW) load_q<DK>(qn, qr, q0 + NW * kQW, d, slq, a.qsign, lane);
 
     f32x16 s[NKT];
     float mx = -__builtin_inff();
@@ -1067,10 +1076,10 @@ void attn_short(Args16 a) {
       }
     }
     if constexpr (kStaged)
-      store_out_staged<DK, OUT_F32, H>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane,
+      store_out_staged<DK, OUT_F32, H>(o, lsum, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane,
                                     stage);
     else
-      store_out<DK, OUT_F32, H>(o, lsum, a.out, (size_t)bh * Lq * d, q0, Lq, d, lane);
+      store_out<DK, OUT_F32, H>(o, lsum, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
     if (t + 1 < QPW) {
 #pragma unroll
       for (int dk = 0; dk < DK / 16; ++dk) qf[dk] = qn[dk];

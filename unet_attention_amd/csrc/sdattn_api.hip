@@ -70,35 +70,77 @@ bool f32_out(int dtype) {
          dtype == SDATTN_DTYPE_F16_F32OUT;
 }
 
+// Row strides of a call: 0 = contiguous [B, H, L, d]; otherwise token-major
+// [B, L, ld] operands with head h in columns [h*d, h*d + d).
+struct Strides {
+  int ldq = 0, ldkv = 0, ldo = 0;
+  bool token_major() const { return ldq != 0; }
+};
+
+sdattn::Layout layout_of(int H, int L, int d, int ld) {
+  sdattn::Layout l;
+  if (ld == 0) {
+    l.sb = (long long)H * L * d;
+    l.sh = L * d;
+    l.sl = d;
+  } else {
+    l.sb = (long long)L * ld;
+    l.sh = d;
+    l.sl = ld;
+  }
+  return l;
+}
+
+// Elements from an operand's base to the end of its last element.
+int64_t span_elems(int B, int H, int L, int d, int ld) {
+  if (ld == 0) return (int64_t)B * H * L * d;
+  return ((int64_t)B * L - 1) * ld + (int64_t)H * d;
+}
+
 int validate(const void *q, const void *k, const void *v, void *out, int B,
-             int H, int Lq, int Lk, int d, float scale, int dtype) {
+             int H, int Lq, int Lk, int d, float scale, int dtype, const Strides &st) {
   if (!known_dtype(dtype)) return SDATTN_ERR_INVALID_ARG;
   if (!q || !k || !v || !out) return SDATTN_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || Lq < 1 || Lk < 1 || d < 1) return SDATTN_ERR_INVALID_ARG;
   if (!isfinite(scale)) return SDATTN_ERR_INVALID_ARG;
-  const int64_t nq = (int64_t)B * H * Lq * d, nk = (int64_t)B * H * Lk * d;
-  if (nq > INT32_MAX || nk > INT32_MAX) return SDATTN_ERR_INVALID_ARG;
+  if (st.token_major()) {
+    // every row holds all heads; rows start 16-byte aligned
+    const int64_t hd = (int64_t)H * d;
+    for (int ld : {st.ldq, st.ldkv, st.ldo})
+      if (ld < hd || ld % 8 != 0) return SDATTN_ERR_INVALID_ARG;
+  }
+  const int64_t nq = span_elems(B, H, Lq, d, st.ldq);
+  const int64_t nk = span_elems(B, H, Lk, d, st.ldkv);
+  const int64_t no = span_elems(B, H, Lq, d, st.ldo);
+  if (nq > INT32_MAX || nk > INT32_MAX || no > INT32_MAX) return SDATTN_ERR_INVALID_ARG;
+  // Kernels address a head's rows, and up to 64 rows past its end (read as
+  // zero by the range check), with 32-bit byte offsets.
+  const int64_t slq = st.ldq ? st.ldq : d, slk = st.ldkv ? st.ldkv : d;
+  if ((Lq + 64) * slq > INT32_MAX || (Lk + 64) * slk > INT32_MAX) return SDATTN_ERR_INVALID_ARG;
   if (d % 8 != 0 || d > 256) return SDATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return SDATTN_ERR_MISALIGNED;
   const int64_t ein = (dtype == SDATTN_DTYPE_F32) ? 4 : 2;
   const int64_t eout = f32_out(dtype) ? 4 : 2;
-  const int64_t nout = nq * eout;
-  if (overlaps(out, nout, q, nq * ein) || overlaps(out, nout, k, nk * ein) ||
-      overlaps(out, nout, v, nk * ein))
+  if (overlaps(out, no * eout, q, nq * ein) || overlaps(out, no * eout, k, nk * ein) ||
+      overlaps(out, no * eout, v, nk * ein))
     return SDATTN_ERR_INVALID_ARG;
   return SDATTN_OK;
 }
 
 int run(const void *q, const void *k, const void *v, void *out, int B, int H,
-        int Lq, int Lk, int d, float scale, int dtype, void *stream, Path path) {
-  int rc = validate(q, k, v, out, B, H, Lq, Lk, d, scale, dtype);
+        int Lq, int Lk, int d, float scale, int dtype, void *stream, Path path,
+        const Strides &st = Strides()) {
+  int rc = validate(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, st);
   if (rc != SDATTN_OK) return rc;
   const int cap = sdattn::short_path_max_keys(d);
   if (path == Path::Short && Lk > cap) return SDATTN_ERR_UNSUPPORTED;
   rc = check_device();
   if (rc != SDATTN_OK) return rc;
 
+  const sdattn::Layout lq = layout_of(H, Lq, d, st.ldq);
+  const sdattn::Layout lk = layout_of(H, Lk, d, st.ldkv);
+  const sdattn::Layout lo = layout_of(H, Lq, d, st.ldo);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (dtype == SDATTN_DTYPE_F32) {
@@ -107,6 +149,10 @@ int run(const void *q, const void *k, const void *v, void *out, int B, int H,
     a.k = static_cast<const float *>(k);
     a.v = static_cast<const float *>(v);
     a.out = static_cast<float *>(out);
+    a.H = H;
+    a.lq = lq;
+    a.lk = lk;
+    a.lo = lo;
     a.Lq = Lq;
     a.Lk = Lk;
     a.d = d;
@@ -118,6 +164,10 @@ int run(const void *q, const void *k, const void *v, void *out, int B, int H,
     a.k = static_cast<const uint16_t *>(k);
     a.v = static_cast<const uint16_t *>(v);
     a.out = out;
+    a.H = H;
+    a.lq = lq;
+    a.lk = lk;
+    a.lo = lo;
     a.Lq = Lq;
     a.Lk = Lk;
     a.d = d;
@@ -153,6 +203,17 @@ int sdattn_stream_fwd(const void *q, const void *k, const void *v, void *out,
   return run(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, stream, Path::Stream);
 }
 
+int sdattn_fwd_strided(const void *q, const void *k, const void *v, void *out, int B,
+                       int H, int Lq, int Lk, int d, int ldq, int ldkv, int ldo,
+                       float scale, int dtype, void *stream) {
+  Strides st;
+  st.ldq = ldq;
+  st.ldkv = ldkv;
+  st.ldo = ldo;
+  if (ldq <= 0 || ldkv <= 0 || ldo <= 0) return SDATTN_ERR_INVALID_ARG;
+  return run(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, stream, Path::Auto, st);
+}
+
 int sdattn_cross_max_ctx(int d, int dtype) {
   if (!known_dtype(dtype)) return 0;
   if (d < 8 || d > 256 || d % 8 != 0) return 0;
@@ -171,6 +232,6 @@ const char *sdattn_strerror(int status) {
   }
 }
 
-int sdattn_version(void) { return 10100; }
+int sdattn_version(void) { return 10200; }
 
 }  // extern "C"
