@@ -1,14 +1,15 @@
-"""Plain fp64 CPU oracle for scaled dot-product attention.
+"""Plain fp64 CPU oracles for scaled dot-product attention and GroupNorm.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py`` may import this package.  It shares
 no code with the HIP library and imports nothing from it.
 
-The arithmetic lives in ``attn_oracle.c`` (the plain definition of
+The arithmetic lives in C: ``attn_oracle.c`` (the plain definition of
 ``O = softmax(sigma * Q K^T) V`` from the page "Diffusion inference engine
 from scratch: Rust + wgpu", section 3.2, evaluated row by row in IEEE double
-with sequential sums).  This module only compiles it with gcc and marshals
-numpy arrays through ctypes.
+with sequential sums) and ``group_norm_oracle.c`` (the same page's section
+3.1 GroupNorm, two-pass mean and variance per group, optional SiLU).  This
+module only compiles them with gcc and marshals numpy arrays through ctypes.
 """
 from __future__ import annotations
 
@@ -21,6 +22,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "attn_oracle.c")
 LIB = os.path.join(_HERE, "liboracle.so")
+GN_SRC = os.path.join(_HERE, "group_norm_oracle.c")
+GN_LIB = os.path.join(_HERE, "liboracle_gn.so")
 
 # -O2, no -ffast-math and no FP contraction: sequential, reproducible sums.
 CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
@@ -143,3 +146,52 @@ def attn_rows(q, k, v, scale, rows, nthreads=0):
 
 def attn_probs(q, k, v, scale):
     return get().attn_probs(q, k, v, scale)
+
+
+# ---------------------------------------------------------------------------
+# GroupNorm (+ SiLU)
+
+class GroupNormOracle:
+    """ctypes handle on one compiled copy of ``group_norm_oracle.c``."""
+
+    def __init__(self, path: str = GN_LIB):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.oracle_group_norm_f64.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64,
+                                              ctypes.c_double, ctypes.c_int, ctypes.c_int]
+        lib.oracle_group_norm_f64.restype = ctypes.c_int
+        self._lib = lib
+
+    def group_norm(self, x, gamma, beta, groups: int, eps: float, silu: bool = False,
+                   nthreads: int = 0) -> np.ndarray:
+        """x: [N, C, ...] (trailing dims flattened); gamma, beta: [C]."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        N, C = x.shape[0], x.shape[1]
+        S = int(np.prod(x.shape[2:])) if x.ndim > 2 else 1
+        g = np.ascontiguousarray(gamma, dtype=np.float64).reshape(-1)
+        b = np.ascontiguousarray(beta, dtype=np.float64).reshape(-1)
+        if g.size != C or b.size != C:
+            raise ValueError("gamma and beta must have C entries")
+        y = np.empty_like(x)
+        rc = self._lib.oracle_group_norm_f64(_ptr(x), _ptr(g), _ptr(b), _ptr(y), N, C, S,
+                                             groups, float(eps), int(bool(silu)), nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle_group_norm_f64 failed ({rc})")
+        return y
+
+
+_default_gn: GroupNormOracle | None = None
+
+
+def get_gn() -> GroupNormOracle:
+    """The GroupNorm oracle built from this directory's source."""
+    global _default_gn
+    if _default_gn is None:
+        if not os.path.exists(GN_LIB) or os.path.getmtime(GN_LIB) < os.path.getmtime(GN_SRC):
+            build(GN_SRC, GN_LIB)
+        _default_gn = GroupNormOracle(GN_LIB)
+    return _default_gn
+
+
+def group_norm(x, gamma, beta, groups, eps, silu=False, nthreads=0):
+    return get_gn().group_norm(x, gamma, beta, groups, eps, silu, nthreads)
