@@ -37,7 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from workloads import WORKLOADS, make_inputs  # noqa: E402
+from workloads import GN_WORKLOADS, WORKLOADS, make_gn_inputs, make_inputs  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 (and fp16) MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
@@ -84,7 +84,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="sd15_64x64_block", choices=sorted(STEPS))
+    ap.add_argument("--workload", default="sd15_64x64_block",
+                    choices=sorted(STEPS) + sorted(f"gn_{n}" for n in GN_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -118,6 +119,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload.startswith("gn_"):
+        bench_group_norm(args, args.workload[3:])
+        return
     if args.copy_calibration:
         copy_calibration()
         return
@@ -291,6 +295,91 @@ def cpu_baseline(args, calls, ws, inputs, set0, step_flops):
            "sample": f"one full step ({' + '.join(w.name for w in ws)}), fp64, "
                      f"{total:.2f} s on {threads} threads of {model}"}
     return cpu, worst
+
+
+def bench_group_norm(args, name):
+    """GroupNorm (+ SiLU) of one UNet level: an HBM-bound kernel, measured in
+    GB/s of algorithmic traffic (x read once, y written once, gamma/beta)."""
+    import torch
+    import unet_attention_amd as sd
+    w = GN_WORKLOADS[name]
+    x = make_gn_inputs(w)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    code = {"bf16": sd.SDATTN_DTYPE_BF16, "f16": sd.SDATTN_DTYPE_F16,
+            "f32": sd.SDATTN_DTYPE_F32}[w.dtype]
+    if w.dtype == "f32":
+        x0 = torch.from_numpy(np.ascontiguousarray(x.x)).to(dev)
+    else:
+        x0 = torch.from_numpy(np.ascontiguousarray(x.x_bits).view(np.int16)).view(tdt).to(dev)
+    g = torch.from_numpy(x.gamma).to(dev)
+    b = torch.from_numpy(x.beta).to(dev)
+    set_bytes = 2 * x0.numel() * x0.element_size()
+    nsets = max(2, -(-ROTATE_BYTES // set_bytes))
+    sets = [(x0 if s == 0 else x0.clone(), torch.empty_like(x0)) for s in range(nsets)]
+    torch.cuda.synchronize()
+    fn = sd.load().sdattn_group_norm
+
+    def launch(xx, yy):
+        rc = fn(xx.data_ptr(), g.data_ptr(), b.data_ptr(), yy.data_ptr(), w.N, w.C, w.HW, w.G,
+                w.eps, int(w.silu), code, sh)
+        if rc != sd.SDATTN_OK:
+            raise sd.SdattnError(rc, "bench group norm")
+
+    for i in range(args.warmup):
+        launch(*sets[i % nsets])
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        launch(*sets[i % nsets])
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / K
+    per_ms = float(np.mean([a.elapsed_time(c) for a, c in ev]))
+    nbytes = w.bytes_alg()
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    ach = nbytes / (per_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": load_traffic(args.workload, name),
+            "kernel": f"sdattn_group_norm N{w.N} C{w.C} HW{w.HW} G{w.G}",
+            "alg_bytes_per_launch": nbytes, "us_per_launch": round(per_ms * 1e3, 3)}
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        t = time.perf_counter()
+        want = oracle.group_norm(x.x, x.gamma, x.beta, w.G, w.eps, w.silu, nthreads=threads)
+        el = time.perf_counter() - t
+        got = sets[0][1].float().cpu().numpy().astype(np.float64)
+        e = np.abs(got - want)
+        parity = {name: {"max_abs": float(e.max()), "mean_abs": float(e.mean())}}
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                         "?")
+        cpu = {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle", "sample": f"the whole workload {name}, fp64, {el:.3f} s on "
+                                           f"{threads} threads of {model}"}
+    line = {
+        "metric": "GroupNorm+SiLU GB/s (x read once, y written once)", "value": round(value, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "shape": f"N{w.N} C{w.C} H{w.H} W{w.W} G{w.G}",
+                   "silu": w.silu, "eps": w.eps, "buffer_sets_rotated": nsets,
+                   "rotated_bytes": nsets * set_bytes},
+        "roofline": roof, "cpu_baseline": cpu, "parity_vs_oracle": parity,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

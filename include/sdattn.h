@@ -1,6 +1,7 @@
 /*
  * sdattn.h -- C ABI of libsdattn: fused scaled dot-product attention for the
- * transformer blocks of a diffusion UNet, on AMD MI355X (gfx950).
+ * transformer blocks of a diffusion UNet, and the GroupNorm(+SiLU) of its
+ * residual blocks, on AMD MI355X (gfx950).
  *
  * Operation.  For every batch b < B, head h < H and query row i < Lq:
  *
@@ -113,6 +114,30 @@ int sdattn_fwd_strided(const void *q, const void *k, const void *v, void *out,
                        int B, int H, int Lq, int Lk, int d, int ldq, int ldkv,
                        int ldo, float scale, int dtype, void *stream);
 
+/* GroupNorm, optionally fused with the SiLU that follows it: the page's
+ * section 3.1 normalisation (each group's mean and variance, inverse
+ * standard deviation 1/sqrt(var + eps)) with the GroupNorm + SiLU fusion its
+ * model-level optimisation list names.  x and y are contiguous [N, C, HW]
+ * (NCHW with HW = H*W); the G groups are C/G consecutive channels each; for
+ * every sample n and group g with M = (C/G)*HW elements:
+ *
+ *     mu = mean(x over the group),  var = mean((x - mu)^2)   (population)
+ *     y  = (x - mu) / sqrt(var + eps) * gamma[c] + beta[c]
+ *     y  = y / (1 + exp(-y))                                  if silu == 1
+ *
+ * gamma and beta are fp32 device arrays of C values.  dtype (as above)
+ * gives x's type and y's: fp32/fp32, bf16/bf16, bf16/fp32, fp16/fp16,
+ * fp16/fp32; statistics and arithmetic are fp32.  y == x (in place) is
+ * allowed when both have the same element size; any other overlap of y with
+ * x, gamma or beta is SDATTN_ERR_INVALID_ARG, as are N, C, HW, G < 1,
+ * C % G != 0, a non-finite or negative eps and silu not 0/1.  HW % 8 != 0
+ * or more than 8192 channels per group is SDATTN_ERR_UNSUPPORTED; x and y
+ * must be 16-byte aligned, gamma and beta 4-byte aligned
+ * (SDATTN_ERR_MISALIGNED). */
+int sdattn_group_norm(const void *x, const float *gamma, const float *beta, void *y,
+                      int N, int C, int HW, int G, float eps, int silu, int dtype,
+                      void *stream);
+
 /* Largest context length the short-key path accepts for this head dim and
  * dtype; 0 if (d, dtype) is unsupported. */
 int sdattn_cross_max_ctx(int d, int dtype);
@@ -120,8 +145,8 @@ int sdattn_cross_max_ctx(int d, int dtype);
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *sdattn_strerror(int status);
 
-/* ABI version: major * 10000 + minor * 100 + patch (1.2: fp16 dtypes and
- * sdattn_fwd_strided). */
+/* ABI version: major * 10000 + minor * 100 + patch (1.3: fp16 dtypes,
+ * sdattn_fwd_strided, sdattn_group_norm). */
 int sdattn_version(void);
 
 #ifdef __cplusplus

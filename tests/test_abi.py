@@ -38,7 +38,7 @@ def test_exports_every_header_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert sd.sdattn_version() == 10200
+    assert sd.sdattn_version() == 10300
     seen = set()
     for code in range(6):
         msg = sd.sdattn_strerror(code)
@@ -174,3 +174,56 @@ def test_strided_valid_call_without_gpu_reports_device(lib, dtype):
     # fused projection layout: k and v are column slices of q's rows
     assert call_strided(k=Q + 2 * 320, v=Q + 4 * 320, ldq=960, ldkv=960, Lk=64,
                         dtype=dtype) == sd.SDATTN_ERR_DEVICE
+
+
+# --------------------------------------------------------------------------
+# GroupNorm entry: host-side validation
+
+X, GA, BE, Y = 0x10000000, 0x70000000, 0x70010000, 0x40000000
+
+
+def call_gn(**kw):
+    args = dict(x=X, gamma=GA, beta=BE, y=Y, N=2, C=320, HW=4096, G=32, eps=1e-5, silu=1,
+                dtype=sd.SDATTN_DTYPE_BF16, stream=None)
+    args.update(kw)
+    return sd.sdattn_group_norm(*(args[n] for n in (
+        "x", "gamma", "beta", "y", "N", "C", "HW", "G", "eps", "silu", "dtype", "stream")))
+
+
+BAD_GN = [
+    ("null_x", dict(x=None), sd.SDATTN_ERR_INVALID_ARG),
+    ("null_gamma", dict(gamma=None), sd.SDATTN_ERR_INVALID_ARG),
+    ("null_y", dict(y=None), sd.SDATTN_ERR_INVALID_ARG),
+    ("N0", dict(N=0), sd.SDATTN_ERR_INVALID_ARG),
+    ("G0", dict(G=0), sd.SDATTN_ERR_INVALID_ARG),
+    ("C_not_multiple_of_G", dict(C=330), sd.SDATTN_ERR_INVALID_ARG),
+    ("eps_negative", dict(eps=-1e-5), sd.SDATTN_ERR_INVALID_ARG),
+    ("eps_nan", dict(eps=float("nan")), sd.SDATTN_ERR_INVALID_ARG),
+    ("silu_2", dict(silu=2), sd.SDATTN_ERR_INVALID_ARG),
+    ("dtype", dict(dtype=9), sd.SDATTN_ERR_INVALID_ARG),
+    ("too_big", dict(N=1 << 10, HW=1 << 20), sd.SDATTN_ERR_INVALID_ARG),
+    ("HW_not_multiple_of_8", dict(HW=4092), sd.SDATTN_ERR_UNSUPPORTED),
+    ("too_many_channels_per_group", dict(C=16384, G=1, HW=8), sd.SDATTN_ERR_UNSUPPORTED),
+    ("misaligned_x", dict(x=X + 2), sd.SDATTN_ERR_MISALIGNED),
+    ("misaligned_y", dict(y=Y + 8), sd.SDATTN_ERR_MISALIGNED),
+    ("misaligned_gamma", dict(gamma=GA + 2), sd.SDATTN_ERR_MISALIGNED),
+    ("y_overlaps_x", dict(y=X + 64), sd.SDATTN_ERR_INVALID_ARG),
+    ("in_place_with_fp32_out", dict(y=X, dtype=sd.SDATTN_DTYPE_BF16_F32OUT),
+     sd.SDATTN_ERR_INVALID_ARG),
+    ("y_overlaps_beta", dict(y=BE - 16), sd.SDATTN_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("case", BAD_GN, ids=[b[0] for b in BAD_GN])
+def test_group_norm_invalid_arguments(lib, case):
+    _, kw, want = case
+    assert call_gn(**kw) == want
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2, 3, 4])
+def test_group_norm_valid_call_without_gpu_reports_device(lib, dtype):
+    if _gpu_present():
+        pytest.skip("a GPU is present; fake pointers must not reach a launch")
+    assert call_gn(dtype=dtype) == sd.SDATTN_ERR_DEVICE
+    if dtype in (0, 1, 3):   # same element size in and out: in place is allowed
+        assert call_gn(dtype=dtype, y=X) == sd.SDATTN_ERR_DEVICE

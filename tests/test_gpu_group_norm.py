@@ -1,0 +1,127 @@
+"""GroupNorm (+ SiLU) on the GPU (through the C ABI) against the fp64 CPU
+oracle.  Every test needs an MI355X; all are marked ``gpu``.  Inputs come
+from the seeded generator in ``workloads``; expected values only from the
+oracle.
+
+Gate: statistics and arithmetic are fp32 on exact stored inputs, so an
+fp32 output must match within 1e-4 absolute (outputs are O(1)-O(10)); a
+16-bit output adds its own rounding, half an ulp of the output type.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import half_ulp_bf16, half_ulp_f16, say
+from workloads import GN_WORKLOADS, make_gn_inputs
+
+pytestmark = pytest.mark.gpu
+
+GN_F32_MAX = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import unet_attention_amd as sd
+    sd.load()
+    return "cuda"
+
+
+def _device_x(x, dev):
+    import torch
+    if x.w.dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x.x)).to(dev)
+    tdt = torch.bfloat16 if x.w.dtype == "bf16" else torch.float16
+    return torch.from_numpy(np.ascontiguousarray(x.x_bits).view(np.int16)).view(tdt).to(dev)
+
+
+def _check(got, want, out, what):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    e = np.abs(got - want)
+    if out == "f32":
+        h = 0.0
+    else:
+        h = half_ulp_bf16(want) if out == "bf16" else half_ulp_f16(want)
+    worst = float((e - h).max())
+    assert worst <= GN_F32_MAX, f"{what}: max(|err| - ulp/2) {worst:.3e} > {GN_F32_MAX}"
+
+
+def _run(w, x, dev, out_dtype=None, out=None):
+    import torch
+    import unet_attention_amd as sd
+    tx = _device_x(x, dev) if out is None else out
+    g = torch.from_numpy(x.gamma).to(dev)
+    b = torch.from_numpy(x.beta).to(dev)
+    y = sd.group_norm(tx, g, b, w.G, eps=w.eps, silu=w.silu, out_dtype=out_dtype,
+                      out=out)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("silu", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("name", sorted(GN_WORKLOADS))
+def test_group_norm_workloads(dev, name, dtype, silu):
+    import torch
+    w = GN_WORKLOADS[name].with_(dtype=dtype, silu=silu)
+    x = make_gn_inputs(w)
+    want = oracle.group_norm(x.x, x.gamma, x.beta, w.G, w.eps, silu).astype(np.float64)
+    outs = [("f32", torch.float32)] + ([] if dtype == "f32" else
+                                       [(dtype, torch.bfloat16 if dtype == "bf16" else torch.float16)])
+    for oname, odt in outs:
+        say(f"group norm {name} {dtype}->{oname} silu={silu} {w}")
+        y = _run(w, x, dev, out_dtype=odt)
+        got = y.float().cpu().numpy().astype(np.float64)
+        say(f"group norm {name} {dtype}->{oname} max err {np.abs(got - want).max():.3e}")
+        _check(got, want, oname, f"{name} {dtype}->{oname} silu={silu}")
+
+
+@pytest.mark.parametrize("N,C,H,W,G", [(3, 12, 4, 6, 4), (1, 8, 8, 1, 8), (2, 64, 2, 4, 1),
+                                       (1, 4, 128, 136, 2)])
+def test_group_norm_odd_shapes(dev, N, C, H, W, G):
+    """Groups of one channel, one group over all channels, chunk counts that
+    do not fill the workgroup, and a 34816-element group (register path
+    near its widest tile count)."""
+    from workloads import GnWorkload
+    w = GnWorkload("odd", N, C, H, W, G, "bf16", 7100 + N * C + H * W + G)
+    x = make_gn_inputs(w)
+    want = oracle.group_norm(x.x, x.gamma, x.beta, G, w.eps, w.silu)
+    import torch
+    say(f"group norm odd {w}")
+    got = _run(w, x, dev, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    _check(got, want, "f32", f"odd {N},{C},{H},{W},{G}")
+
+
+@pytest.mark.parametrize("name", ["gn8", "gn64", "gn128"])
+def test_group_norm_in_place(dev, name):
+    """y = x (one workgroup per group: register-resident, or streaming for
+    gn128) against the oracle, like the out-of-place (split) result."""
+    w = GN_WORKLOADS[name]
+    x = make_gn_inputs(w)
+    want = oracle.group_norm(x.x, x.gamma, x.beta, w.G, w.eps, w.silu)
+    t = _device_x(x, dev)
+    say(f"group norm in place {name}")
+    got = _run(w, x, dev, out=t)
+    assert got.data_ptr() == t.data_ptr()
+    _check(got.float().cpu().numpy().astype(np.float64), want, w.dtype, f"in place {name}")
+
+
+def test_group_norm_constant_groups_give_beta(dev):
+    """Constant groups have zero deviation: y = beta (to fp32 rounding of
+    the folded scale and shift)."""
+    import torch
+    import unet_attention_amd as sd
+    N, C, HW, G = 2, 64, 1024, 32
+    vals = 1.5 + np.repeat(np.arange(N * G, dtype=np.float32), C // G * HW).reshape(N, C, HW)
+    x = torch.from_numpy(vals).to(dev)
+    beta = torch.linspace(-2, 2, C, device=dev)
+    gamma = torch.linspace(0.5, 1.5, C, device=dev)
+    say("group norm constant groups")
+    y = sd.group_norm(x, gamma, beta, G, eps=1e-5, silu=False)
+    torch.cuda.synchronize()
+    err = (y - beta[None, :, None]).abs().max().item()
+    assert err <= 1e-5, f"constant groups: {err:.3e}"

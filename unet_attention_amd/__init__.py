@@ -42,6 +42,7 @@ EXPORTS = {
     "sdattn_stream_fwd": (_I, _ATTN_ARGS),
     "sdattn_fwd_strided": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I,
                                 ctypes.c_float, _I, _VP]),
+    "sdattn_group_norm": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _I, _VP]),
     "sdattn_cross_max_ctx": (_I, [_I, _I]),
     "sdattn_strerror": (ctypes.c_char_p, [_I]),
     "sdattn_version": (_I, []),
@@ -93,6 +94,10 @@ def sdattn_stream_fwd(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, stream):
 def sdattn_fwd_strided(q, k, v, out, B, H, Lq, Lk, d, ldq, ldkv, ldo, scale, dtype, stream):
     return load().sdattn_fwd_strided(q, k, v, out, B, H, Lq, Lk, d, ldq, ldkv, ldo,
                                      scale, dtype, stream)
+
+
+def sdattn_group_norm(x, gamma, beta, y, N, C, HW, G, eps, silu, dtype, stream):
+    return load().sdattn_group_norm(x, gamma, beta, y, N, C, HW, G, eps, silu, dtype, stream)
 
 
 def sdattn_cross_max_ctx(d, dtype):
@@ -216,4 +221,33 @@ def fwd_tokens(q, k, v, heads, out=None, scale=None, out_dtype=None, stream=None
                                    out.stride(1), scale, dtype_code, stream)
     if rc != SDATTN_OK:
         raise SdattnError(rc, "sdattn_fwd_strided")
+    return out
+
+
+def group_norm(x, gamma, beta, groups, eps=1e-5, silu=False, out=None, out_dtype=None,
+               stream=None):
+    """GroupNorm (+ SiLU) of a contiguous [N, C, *spatial] device tensor via
+    sdattn_group_norm; gamma and beta are [C] (passed as fp32).  out may be
+    x itself (in place) when the output dtype equals the input dtype."""
+    import torch
+    dtype_code, odt = _dtype_code(x.dtype, out_dtype)
+    if not x.is_cuda or not x.is_contiguous() or x.dim() < 2:
+        raise ValueError("x must be a contiguous [N, C, ...] device tensor")
+    N, C = x.shape[0], x.shape[1]
+    HW = x.numel() // max(1, N * C)
+    g = gamma.to(device=x.device, dtype=torch.float32).contiguous()
+    b = beta.to(device=x.device, dtype=torch.float32).contiguous()
+    if g.numel() != C or b.numel() != C:
+        raise ValueError("gamma and beta must have C entries")
+    if out is None:
+        out = torch.empty(x.shape, dtype=odt, device=x.device)
+    elif out.dtype != odt or out.shape != x.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of x's shape and the output dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = load().sdattn_group_norm(x.data_ptr(), g.data_ptr(), b.data_ptr(), out.data_ptr(),
+                                  N, C, HW, groups, float(eps), int(bool(silu)), dtype_code,
+                                  stream)
+    if rc != SDATTN_OK:
+        raise SdattnError(rc, "sdattn_group_norm")
     return out

@@ -69,6 +69,19 @@ struct F32Args {
   float scale;
 };
 
+// GroupNorm (+ SiLU): x, y are [N, C, S] contiguous (S = H*W), G groups of
+// C/G consecutive channels, per-channel fp32 gamma and beta.
+struct GnArgs {
+  const void *x;
+  const float *gamma;
+  const float *beta;
+  void *y;
+  int N, C, S, G;
+  float eps;
+  int silu;
+  int split;  // workgroups per group (1: the group's own workgroup only)
+};
+
 // The dispatcher hands workgroup i to XCD (i mod 8).  Renumber so that the
 // workgroups resident on one XCD get consecutive logical ids, i.e. the
 // query blocks of one (b, h) share that XCD's L2 copy of its K and V.

@@ -17,6 +17,15 @@ int short_path_max_keys(int d);
 hipError_t launch_16(const Args16 &a, int BH, bool short_path, bool out_f32, bool half,
                      hipStream_t stream);
 
+// GroupNorm (+ SiLU); elem: 0 fp32, 1 bf16, 2 fp16 (x, and y unless out_f32).
+hipError_t launch_group_norm(const GnArgs &a, int elem, bool out_f32, hipStream_t stream);
+
+// Largest group (elements) the register-resident GroupNorm kernel holds.
+int group_norm_max_resident();
+
+// Most channels per group (their gamma and beta are staged in LDS).
+int group_norm_max_channels_per_group();
+
 // fp32 kernel (any Lk).
 hipError_t launch_f32(const F32Args &a, int BH, hipStream_t stream);
 

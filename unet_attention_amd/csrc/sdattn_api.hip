@@ -1,10 +1,11 @@
 // sdattn_api.hip -- the C ABI declared in include/sdattn.h: argument
 // validation (host only, before any HIP call), device check, dispatch to
-// the kernels, launch on the caller's stream.
+// the kernels (attention and GroupNorm), launch on the caller's stream.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "launch.hpp"
@@ -13,6 +14,10 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
+#ifndef SDATTN_GN_TARGET_WGS
+#define SDATTN_GN_TARGET_WGS 256  // one workgroup per MI355X CU
+#endif
+constexpr int64_t kGroupNormTargetWgs = SDATTN_GN_TARGET_WGS;
 
 struct DeviceInfo {
   std::once_flag once;
@@ -214,6 +219,52 @@ int sdattn_fwd_strided(const void *q, const void *k, const void *v, void *out, i
   return run(q, k, v, out, B, H, Lq, Lk, d, scale, dtype, stream, Path::Auto, st);
 }
 
+int sdattn_group_norm(const void *x, const float *gamma, const float *beta, void *y,
+                      int N, int C, int HW, int G, float eps, int silu, int dtype,
+                      void *stream) {
+  if (!known_dtype(dtype)) return SDATTN_ERR_INVALID_ARG;
+  if (!x || !gamma || !beta || !y) return SDATTN_ERR_INVALID_ARG;
+  if (N < 1 || C < 1 || HW < 1 || G < 1 || C % G != 0) return SDATTN_ERR_INVALID_ARG;
+  if (!isfinite(eps) || eps < 0.f || (silu != 0 && silu != 1)) return SDATTN_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)N * C * HW;
+  if (n > INT32_MAX || (int64_t)N * G > INT32_MAX) return SDATTN_ERR_INVALID_ARG;
+  if (HW % 8 != 0 || C / G > sdattn::group_norm_max_channels_per_group())
+    return SDATTN_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(y) || (reinterpret_cast<uintptr_t>(gamma) & 3u) ||
+      (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return SDATTN_ERR_MISALIGNED;
+  const int64_t ein = (dtype == SDATTN_DTYPE_F32) ? 4 : 2;
+  const int64_t eout = f32_out(dtype) ? 4 : 2;
+  // In place (y == x) is allowed when input and output elements have the
+  // same size: every element is read before the workgroup writes it.
+  const bool in_place = (x == y) && ein == eout;
+  if (!in_place && overlaps(y, n * eout, x, n * ein)) return SDATTN_ERR_INVALID_ARG;
+  if (overlaps(y, n * eout, gamma, (int64_t)C * 4) || overlaps(y, n * eout, beta, (int64_t)C * 4))
+    return SDATTN_ERR_INVALID_ARG;
+  int rc = check_device();
+  if (rc != SDATTN_OK) return rc;
+  sdattn::GnArgs a{};
+  a.x = x;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.y = y;
+  a.N = N;
+  a.C = C;
+  a.S = HW;
+  a.G = G;
+  a.eps = eps;
+  a.silu = silu;
+  // Out of place with fewer groups than CUs: spread each group over up to 8
+  // workgroups (in place keeps one workgroup per group).
+  a.split = 1;
+  if (!in_place && (int64_t)N * G < kGroupNormTargetWgs)
+    a.split = (int)std::min<int64_t>(8, kGroupNormTargetWgs / ((int64_t)N * G));
+  const int elem = (dtype == SDATTN_DTYPE_F32) ? 0 : half_dtype(dtype) ? 2 : 1;
+  const hipError_t err = sdattn::launch_group_norm(a, elem, f32_out(dtype),
+                                                   static_cast<hipStream_t>(stream));
+  return (err == hipSuccess) ? SDATTN_OK : SDATTN_ERR_LAUNCH;
+}
+
 int sdattn_cross_max_ctx(int d, int dtype) {
   if (!known_dtype(dtype)) return 0;
   if (d < 8 || d > 256 || d % 8 != 0) return 0;
@@ -232,6 +283,6 @@ const char *sdattn_strerror(int status) {
   }
 }
 
-int sdattn_version(void) { return 10200; }
+int sdattn_version(void) { return 10300; }
 
 }  // extern "C"

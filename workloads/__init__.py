@@ -191,3 +191,78 @@ def sample_rows(w: Workload, n: int, seed: int = 7) -> np.ndarray:
         cand |= set(int(x) for x in rng.integers(0, w.Lq, size=per))
         rows |= {base + c for c in cand}
     return np.array(sorted(rows), dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# GroupNorm (+ SiLU) workloads: the UNet's resnet-block activations at each
+# level of SD 1.5 at 512x512 (CFG batch 2, 32 groups), and a 128x128 level
+# (1024x1024 images) whose groups exceed what one workgroup holds on chip.
+# Recipe: rng = default_rng(seed); x = 1.5 + 2 * N(0, 1) as float32 in C
+# order of [N, C, H, W] (a non-zero mean, as activations have), rounded to
+# the storage type like the attention inputs; then gamma = 1 + 0.25 * N(0, 1)
+# and beta = 0.5 * N(0, 1), float32, C values each.
+
+@dataclass(frozen=True)
+class GnWorkload:
+    name: str
+    N: int
+    C: int
+    H: int
+    W: int
+    G: int
+    dtype: str           # "f32", "bf16" or "f16"
+    seed: int
+    eps: float = 1e-5
+    silu: bool = True
+    note: str = field(default="", compare=False)
+
+    @property
+    def HW(self) -> int:
+        return self.H * self.W
+
+    def bytes_alg(self, out_bytes: int | None = None) -> int:
+        """x read once and y written once, plus gamma and beta."""
+        e = 4 if self.dtype == "f32" else 2
+        o = e if out_bytes is None else out_bytes
+        return self.N * self.C * self.HW * (e + o) + 8 * self.C
+
+    def with_(self, **kw) -> "GnWorkload":
+        return replace(self, **kw)
+
+
+GN_WORKLOADS = {
+    "gn64": GnWorkload("gn64", 2, 320, 64, 64, 32, "bf16", 7001,
+                       note="64x64 level, 320 channels"),
+    "gn32": GnWorkload("gn32", 2, 640, 32, 32, 32, "bf16", 7002,
+                       note="32x32 level, 640 channels"),
+    "gn16": GnWorkload("gn16", 2, 1280, 16, 16, 32, "bf16", 7003,
+                       note="16x16 level, 1280 channels"),
+    "gn8": GnWorkload("gn8", 2, 1280, 8, 8, 32, "bf16", 7004,
+                      note="8x8 level, 1280 channels"),
+    "gn128": GnWorkload("gn128", 2, 320, 128, 128, 32, "bf16", 7005,
+                        note="128x128 level (1024x1024 image): 163840-element groups"),
+}
+
+
+@dataclass
+class GnInputs:
+    w: GnWorkload
+    x: np.ndarray                 # float32 values (exactly the stored ones)
+    x_bits: np.ndarray | None     # 16-bit patterns for bf16/f16
+    gamma: np.ndarray
+    beta: np.ndarray
+
+
+def make_gn_inputs(w: GnWorkload) -> GnInputs:
+    rng = np.random.default_rng(w.seed)
+    x = (1.5 + 2.0 * rng.standard_normal((w.N, w.C, w.H, w.W), dtype=np.float32)).astype(np.float32)
+    bits = None
+    if w.dtype == "bf16":
+        bits = round_to_bf16_bits(x)
+        x = bf16_bits_to_f32(bits)
+    elif w.dtype == "f16":
+        x = x.astype(np.float16).astype(np.float32)
+        bits = x.astype(np.float16).view(np.uint16)
+    gamma = (1.0 + 0.25 * rng.standard_normal(w.C)).astype(np.float32)
+    beta = (0.5 * rng.standard_normal(w.C)).astype(np.float32)
+    return GnInputs(w, x, bits, gamma, beta)
