@@ -357,6 +357,23 @@ def test_errors_on_device(dev):
                      torch.zeros(1, 1, cap + 1, 40, dtype=torch.bfloat16, device=dev))
 
 
+@pytest.mark.parametrize("d", [16, 32, 48, 56])
+@pytest.mark.parametrize("Lq,Lk", [(31, 129), (100, 200), (70, 333), (64, 1000)])
+def test_streaming_every_row_layout(dev, Lq, Lk, d):
+    """The streaming kernel for d <= 64 lays out K and V rows per exact head
+    dim (d = DK or DK - 8): the dims the ragged sweep above does not reach."""
+    import torch
+    w = Workload("layout", "self", 1, 2, Lq, Lk, d, "bf16", 7500 + 31 * Lq + Lk + d)
+    x = make_inputs(w)
+    want = oracle.attn(x.q, x.k, x.v, w.scale)
+    q, k, v = to_device(x)
+    say(f"streaming layout Lq={Lq} Lk={Lk} d={d}")
+    assert_bf16_gate(run("stream", q, k, v, w.scale, out_dtype=torch.float32), want,
+                     f"Lq={Lq} Lk={Lk} d={d}")
+    assert_bf16_out_gate(run("stream", q, k, v, w.scale, out_dtype=torch.bfloat16), want,
+                         f"Lq={Lq} Lk={Lk} d={d} bf16out")
+
+
 # ---------------------------------------------------------------------------
 # token-major operands (sdattn_fwd_strided)
 
@@ -369,6 +386,7 @@ def _to_tokens(a):
 
 STRIDED_CASES = [  # (dtype, H, Lq, Lk, d): short-key, fixed-reference, rescaling, fp32
     ("bf16", 2, 129, 77, 40), ("bf16", 3, 300, 300, 64), ("bf16", 2, 100, 333, 80),
+    ("bf16", 3, 100, 300, 40), ("bf16", 2, 70, 200, 56),
     ("f16", 2, 65, 200, 40), ("f32", 2, 33, 77, 40),
 ]
 

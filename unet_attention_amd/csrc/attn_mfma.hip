@@ -624,16 +624,49 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
 #endif
 constexpr int kFixBuffers = SDATTN_FIX_BUFFERS;
 
-template <int DK, int NW, bool OUT_F32>
+// LDS layout of the fixed-reference kernel for head dim D (a multiple of 8,
+// DK = D rounded up to 16): rows as short as the operands allow, so that
+// few transfer lanes carry padding.
+//  * K rows are D elements when D/8 is odd (an odd number of 16-byte chunks
+//    puts the 16-byte reads of consecutive rows on distinct banks), else
+//    D + 8.  With D < DK the reads of columns [D, DK) see the first columns
+//    of the next row, which meet the zero columns of Q; each buffer ends in
+//    a zero chunk for its last row.
+//  * V rows hold D data columns plus, when DV > DK, the chunk with the
+//    ones column.  Transposing reads of columns past that feed rows of O^T
+//    at or beyond D, which are never stored; a row length that is a
+//    multiple of 128 bytes (which would put the four key rows of one read on
+//    the same banks) gets 64 bytes more.
+template <int DK, int D, int NW>
+struct FixPlan {
+  using S = Shape<DK>;
+  static_assert(D % 8 == 0 && D <= DK && D + 16 > DK, "D rounds up to DK");
+  static constexpr int BN = 64;
+  static constexpr int KST = ((D / 8) & 1) ? D : D + 8;
+  static constexpr int KPAD = KST < DK ? 8 : 0;
+  static constexpr int VNEED = D + (S::kOnes ? 8 : 0);
+  static constexpr int VSTR = (VNEED * 2) % 128 == 0 ? VNEED + 32 : VNEED;
+  static constexpr int VTAIL = S::DV > VSTR ? S::DV - VSTR : 0;
+  static constexpr int KCR = KST / 8, VCR = VSTR / 8;
+  static constexpr int KBUF = BN * KST + KPAD;  // elements per K buffer
+  static constexpr int VBUF = BN * VSTR;        // elements per V buffer
+  static constexpr int KI = (BN * KCR + 63) / 64;
+  static constexpr int VI = (BN * VCR + 63) / 64;
+  static constexpr int NI = KI + VI;
+  static constexpr int NIW = (NI + NW - 1) / NW;
+  static_assert((KBUF * 2) % 16 == 0 && (VBUF * 2) % 16 == 0, "16-byte aligned buffers");
+};
+
+template <int DK, int D, int NW, bool OUT_F32>
 __global__ __launch_bounds__(NW * kWave, 2)
 void attn_stream_fix(Args16 a) {
   using S = Shape<DK>;
-  using P = DmaPlan<DK, NW>;
-  static_assert(P::BN == 64 && P::NSUB == 2, "64-key tiles");
+  using P = FixPlan<DK, D, NW>;
   constexpr int BN = P::BN;
   constexpr int NB = kFixBuffers;  // LDS buffers per operand
   static_assert(NB >= 3, "K runs NB tiles ahead, V NB-2 tiles ahead");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[NB * (P::KBUF + P::VBUF)];
+  __shared__ __attribute__((aligned(16))) uint16_t
+      smem[NB * (P::KBUF + P::VBUF) + (P::VTAIL + 7) / 8 * 8];
   uint16_t *const Ks = smem;
   uint16_t *const Vs = smem + NB * P::KBUF;
 
@@ -642,7 +675,7 @@ void attn_stream_fix(Args16 a) {
   const int wg = xcd_remap(blockIdx.x, a.nwg);
   const int bh = wg / a.qblocks;
   const int q0 = (wg - bh * a.qblocks) * (NW * kQW) + wave * kQW;
-  const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
+  const int d = D, Lk = a.Lk, Lq = a.Lq;
   const float c = a.c;
   const int slq = a.lq.sl, slk = a.lk.sl;
   const uint16_t *const kbase = a.k + a.lk.head(bh, a.H);
@@ -670,7 +703,7 @@ void attn_stream_fix(Args16 a) {
     const int cpos = blk * 64 + lane;
     const int cr = isk[r] ? P::KCR : P::VCR;
     const int row = cpos / cr, col = cpos - row * cr;
-    act[r] = (i < P::NI) && row < BN && col < d8;
+    act[r] = (i < P::NI) && row < BN && col < D / 8;
     goff[r] = (uint32_t)(row * slk + col * 8) * 2u;
     loff[r] = (uint32_t)blk * 1024u;
   }
@@ -714,20 +747,17 @@ void attn_stream_fix(Args16 a) {
     if (u >= 2 && u - 2 < n) issue_v(u - 2, u - 2);
   }
 
-  // Constant columns: K [d, DK) zero; V [d, DV) zero with ones at d.
-  if (d8 < S::DK8) {
-    for (int r = tid; r < NB * BN; r += NW * kWave)
-      st16(Ks + r * S::KST + d8 * 8, u32x4{0u, 0u, 0u, 0u});
+  // Constants the transfers never write: the zero chunk after each K buffer
+  // and the V chunk at column D (a one at D, zeros after it).
+  if constexpr (P::KPAD > 0) {
+    if (tid < NB) st16(Ks + tid * P::KBUF + BN * P::KST, u32x4{0u, 0u, 0u, 0u});
   }
-  for (int idx = tid; idx < NB * BN * (S::DV / 8); idx += NW * kWave) {
-    const int r = idx / (S::DV / 8), c8 = idx - r * (S::DV / 8);
-    if (c8 >= d8) {
-      const uint32_t w0 = (S::kOnes && c8 == d8) ? uint32_t(one16<false>()) : 0u;
-      st16(Vs + r * P::VSTR + c8 * 8, u32x4{w0, 0u, 0u, 0u});
-    }
+  if constexpr (S::kOnes) {
+    for (int r = tid; r < NB * BN; r += NW * kWave)
+      st16(Vs + r * P::VSTR + D, u32x4{uint32_t(one16<false>()), 0u, 0u, 0u});
   }
 
-  const int koff = (lane & 31) * S::KST + 8 * (lane >> 5);
+  const int koff = (lane & 31) * P::KST + 8 * (lane >> 5);
   const int g = lane >> 4, pl = lane & 15;
   const int voff = (4 * (g >> 1) + (pl >> 2)) * P::VSTR + 16 * (g & 1) + 4 * (pl & 3);
 
@@ -745,7 +775,7 @@ void attn_stream_fix(Args16 a) {
   auto scores = [&](int b, f32x16 &s0, f32x16 &s1) {
     const uint16_t *kb = Ks + b * P::KBUF + koff;
     s0 = scores_subtile<DK>(kb, qf);
-    s1 = scores_subtile<DK>(kb + 32 * S::KST, qf);
+    s1 = scores_subtile<DK>(kb + 32 * P::KST, qf);
   };
   auto pv = [&](int b, const u32x4 (&pk)[4]) {
     const uint16_t *vb = Vs + b * P::VBUF + voff;
@@ -884,11 +914,15 @@ void attn_stream_fix(Args16 a) {
   } else {
     l = lacc[0];
   }
+  // Rows of O^T at or past D are never stored (some hold sums over padding
+  // or neighbouring LDS rows): only rows < D and l decide the fallback.
   bool ok = __builtin_isfinite(l);
+  const int hb = 4 * (lane >> 5);
 #pragma unroll
   for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ok = ok && __builtin_isfinite(o[mt][i]);
+    for (int i = 0; i < 16; ++i)
+      if (mt * 32 + 8 * (i >> 2) + hb + (i & 3) < D) ok = ok && __builtin_isfinite(o[mt][i]);
   if (__any(!ok)) l = rows_exact<DK>(o, qf, kr, vr, Lk, d, slk, c, lane);
 
   store_out_l<DK, OUT_F32>(o, l, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
@@ -1141,12 +1175,22 @@ void launch_fix(Args16 a, int BH, bool out_f32, hipStream_t stream) {
   constexpr int NW = kStreamFixWaves;
   a.qblocks = (a.Lq + NW * kQW - 1) / (NW * kQW);
   a.nwg = BH * a.qblocks;
-  if (out_f32)
-    hipLaunchKernelGGL((attn_stream_fix<DK, NW, true>), dim3(a.nwg), dim3(NW * kWave), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((attn_stream_fix<DK, NW, false>), dim3(a.nwg), dim3(NW * kWave), 0,
-                       stream, a);
+  // d is DK or DK - 8 (d % 8 == 0); each has its own LDS layout.
+  if (a.d == DK) {
+    if (out_f32)
+      hipLaunchKernelGGL((attn_stream_fix<DK, DK, NW, true>), dim3(a.nwg), dim3(NW * kWave), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((attn_stream_fix<DK, DK, NW, false>), dim3(a.nwg), dim3(NW * kWave),
+                         0, stream, a);
+  } else {
+    if (out_f32)
+      hipLaunchKernelGGL((attn_stream_fix<DK, DK - 8, NW, true>), dim3(a.nwg),
+                         dim3(NW * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_stream_fix<DK, DK - 8, NW, false>), dim3(a.nwg),
+                         dim3(NW * kWave), 0, stream, a);
+  }
 }
 
 // bf16: short-key kernel, else the fixed-reference kernel up to DK 64 and
