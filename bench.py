@@ -176,24 +176,22 @@ def main():
             launch(fn, a)
     torch.cuda.synchronize()
 
-    # timed region: per-kernel events on the launch stream
+    # timed region: one event on the launch stream before every call and one
+    # after the last, so each call is timed between consecutive events (an
+    # event pair around every call would add its own GPU time to the step)
     K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in calls] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    nc = len(calls)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K * nc + 1)]
     torch.cuda.synchronize()
-    t_start.record(stream)
     for i in range(K):
         for j, (fn, a) in enumerate(argv[i % nsets]):
-            ev[i][j][0].record(stream)
+            ev[i * nc + j].record(stream)
             launch(fn, a)
-            ev[i][j][1].record(stream)
-    t_end.record(stream)
+    ev[K * nc].record(stream)
     torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / K
-    per_call_ms = [float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(K)]))
-                   for j in range(len(calls))]
+    ms_step = ev[0].elapsed_time(ev[K * nc]) / K
+    per_call_ms = [float(np.mean([ev[i * nc + j].elapsed_time(ev[i * nc + j + 1])
+                                  for i in range(K)])) for j in range(nc)]
 
     # warm-cache figure: same kernels, one buffer set
     warm_ms = []

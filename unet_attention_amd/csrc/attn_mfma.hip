@@ -331,12 +331,24 @@ struct DmaPlan {
   static constexpr int NIW = (NI + NW - 1) / NW;    // per wave, upper bound
 };
 
-template <int DK, int NW, bool OUT_F32, bool H>
+// KS = 2 splits every 64-key tile between two waves that own the same 32
+// query rows (each takes one 32-key sub-tile): a workgroup then covers
+// NW/2 query blocks, so small problems launch twice as many waves.  Each wave
+// keeps its own running maximum, row sum and O over its keys; the two
+// partial results are merged through LDS at the end (O = a0*O0 + a1*O1,
+// l = a0*l0 + a1*l1 with a_w = 2^(m_w - max(m0, m1))).
+template <int DK, int NW, bool OUT_F32, bool H, int KS = 1>
 __global__ __launch_bounds__(NW * kWave, (waves_per_simd<DK>()))
 void attn_stream_rescale(Args16 a) {
   using S = Shape<DK>;
   using P = DmaPlan<DK, NW>;
   constexpr int BN = P::BN, NSUB = P::NSUB;
+  static_assert(KS == 1 || (KS == 2 && NSUB == 2 && NW % 2 == 0), "two-way split of 64-key tiles");
+  // merge area of the split form: per wave pair, O^T (MT x 16 floats per
+  // lane), then m and l (one float per lane each)
+  constexpr int kMergeFloats = S::MT * 16 * 64 + 2 * 64;
+  static_assert(KS == 1 || (NW / 2) * kMergeFloats * 4 <= P::NB * (P::KBUF + P::VBUF) * 2,
+                "merge area fits in the tile buffers");
   __shared__ __attribute__((aligned(16))) uint16_t smem[P::NB * (P::KBUF + P::VBUF)];
   uint16_t *const Ks = smem;
   uint16_t *const Vs = smem + P::NB * P::KBUF;
@@ -347,7 +359,9 @@ void attn_stream_rescale(Args16 a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = xcd_remap(blockIdx.x, a.nwg);
   const int bh = wg / a.qblocks;
-  const int q0 = (wg - bh * a.qblocks) * (NW * kQW) + wave * kQW;
+  const int qw = wave / KS;         // query block of this wave within the workgroup
+  const int kh = wave - qw * KS;    // its sub-tile of every key tile (split form)
+  const int q0 = (wg - bh * a.qblocks) * (NW / KS * kQW) + qw * kQW;
   const int d = a.d, d8 = d >> 3, Lk = a.Lk, Lq = a.Lq;
   const float c = a.c;
   const int slq = a.lq.sl, slk = a.lk.sl;
@@ -491,10 +505,15 @@ void attn_stream_rescale(Args16 a) {
     if (t + 2 < ntiles) issue(t + 2, (B + 2) % 3);
     const uint16_t *kb = Ks + B * P::KBUF + koff;
     const uint16_t *vb = Vs + B * P::VBUF;
-    f32x16 s0 = scores_subtile<DK, H>(kb, qf), s1;
-    if constexpr (NSUB == 2) s1 = scores_subtile<DK, H>(kb + 32 * S::KST, qf);
-    sub(mask_c, s0, t * BN, vb, 0);
-    if constexpr (NSUB == 2) sub(mask_c, s1, t * BN + 32, vb, 2);
+    if constexpr (KS == 2) {
+      f32x16 s0 = scores_subtile<DK, H>(kb + 32 * kh * S::KST, qf);
+      sub(mask_c, s0, t * BN + 32 * kh, vb, 2 * kh);
+    } else {
+      f32x16 s0 = scores_subtile<DK, H>(kb, qf), s1;
+      if constexpr (NSUB == 2) s1 = scores_subtile<DK, H>(kb + 32 * S::KST, qf);
+      sub(mask_c, s0, t * BN, vb, 0);
+      if constexpr (NSUB == 2) sub(mask_c, s1, t * BN + 32, vb, 2);
+    }
     if (t + 1 < ntiles) vmcnt_barrier_rt<P::NIW>(t + 2 < ntiles ? my_count : 0);
   };
 
@@ -521,7 +540,41 @@ void attn_stream_rescale(Args16 a) {
     step(B0{}, Ragged{}, t);
   }
 
-  store_out<DK, OUT_F32, H>(o, lsum, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
+  if constexpr (KS == 2) {
+    // Every wave is done with the tile buffers (no transfer is in flight
+    // after the last tile); they now hold the second wave's partial result.
+    float *const mg = reinterpret_cast<float *>(smem) + qw * kMergeFloats;
+    const float lw = S::kOnes ? 0.f : sum_halves(lsum);
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mg[(mt * 16 + i) * 64 + lane] = o[mt][i];
+      mg[S::MT * 16 * 64 + lane] = m_run;
+      mg[S::MT * 16 * 64 + 64 + lane] = lw;
+    }
+    __syncthreads();
+    if (kh == 0) {
+      // key 0 is in this wave's half, so m_run is finite; the other half may
+      // have seen no key (m = -inf, O = 0, l = 0): its factor is then 0
+      const float m1 = mg[S::MT * 16 * 64 + lane];
+      const float mx = fmaxf(m_run, m1);
+      const float a0 = fast_exp2(m_run - mx), a1 = fast_exp2(m1 - mx);
+#pragma unroll
+      for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[mt][i] = a0 * o[mt][i] + a1 * mg[(mt * 16 + i) * 64 + lane];
+      if constexpr (S::kOnes) {
+        store_out<DK, OUT_F32, H>(o, 0.f, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
+      } else {
+        const float l = a0 * lw + a1 * mg[S::MT * 16 * 64 + 64 + lane];
+        store_out_l<DK, OUT_F32, H>(o, l, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
+      }
+    }
+  } else {
+    store_out<DK, OUT_F32, H>(o, lsum, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1140,6 +1193,12 @@ void attn_short(Args16 a) {
 constexpr int kStreamFixMaxDk = SDATTN_STREAM_FIX_MAX_DK;  // widest DK of the fixed-reference kernel
 constexpr int kStreamFixWaves = SDATTN_STREAM_FIX_WAVES;
 constexpr int kStreamWaves = SDATTN_STREAM_WAVES;          // rescaling streaming kernel
+// Below this many workgroups of the plain form, the rescaling kernel splits
+// each key tile between two waves (the chip has 256 compute units).
+#ifndef SDATTN_SPLIT_BELOW
+#define SDATTN_SPLIT_BELOW 256
+#endif
+constexpr int kSplitBelow = SDATTN_SPLIT_BELOW;
 constexpr int kShortWaves = SDATTN_SHORT_WAVES;
 constexpr int kShortTiles = SDATTN_SHORT_TILES;   // query tiles per wave (short kernel)
 
@@ -1162,6 +1221,20 @@ void launch_rescale(Args16 a, int BH, bool out_f32, hipStream_t stream) {
   constexpr int NW = kStreamWaves;
   a.qblocks = (a.Lq + NW * kQW - 1) / (NW * kQW);
   a.nwg = BH * a.qblocks;
+  if constexpr (DmaPlan<DK, NW>::NSUB == 2) {
+    if (a.nwg < kSplitBelow) {
+      // few workgroups for the chip: two waves share each query block
+      a.qblocks = (a.Lq + NW / 2 * kQW - 1) / (NW / 2 * kQW);
+      a.nwg = BH * a.qblocks;
+      if (out_f32)
+        hipLaunchKernelGGL((attn_stream_rescale<DK, NW, true, H, 2>), dim3(a.nwg),
+                           dim3(NW * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_stream_rescale<DK, NW, false, H, 2>), dim3(a.nwg),
+                           dim3(NW * kWave), 0, stream, a);
+      return;
+    }
+  }
   if (out_f32)
     hipLaunchKernelGGL((attn_stream_rescale<DK, NW, true, H>), dim3(a.nwg), dim3(NW * kWave), 0,
                        stream, a);
