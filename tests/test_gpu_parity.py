@@ -374,6 +374,19 @@ def test_streaming_every_row_layout(dev, Lq, Lk, d):
                          f"Lq={Lq} Lk={Lk} d={d} bf16out")
 
 
+@pytest.mark.parametrize("d", [80, 160])
+def test_rescaling_unsplit_grid(dev, d):
+    """d > 64 with enough query blocks for the whole chip: the rescaling
+    kernel's plain form (small grids above run its split form)."""
+    import torch
+    w = Workload("unsplit", "self", 2, 8, 4096, 300, d, "bf16", 7700 + d)
+    x = make_inputs(w)
+    want = oracle.attn(x.q, x.k, x.v, w.scale)
+    q, k, v = to_device(x)
+    say(f"rescaling plain grid d={d}")
+    assert_bf16_gate(run("auto", q, k, v, w.scale, out_dtype=torch.float32), want, f"d={d}")
+
+
 # ---------------------------------------------------------------------------
 # token-major operands (sdattn_fwd_strided)
 

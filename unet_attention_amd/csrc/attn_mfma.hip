@@ -921,6 +921,11 @@ void attn_stream_fix(Args16 a) {
     if constexpr (HAS_NEXT) scores(b1, nx0, nx1);
     weights(mask_c, t * BN, cu0, cu1, nmt, pout);
     if constexpr (HAS_PV) pv(b2, pin);
+    // The weights are consumed only in the next iteration.  This opaque use
+    // keeps the compiler from sinking their computation below the next
+    // barrier: it did so in every other iteration, leaving one block with
+    // matrix-core work only and the next with two tiles' vector work.
+    asm volatile("" : "+v"(pout[0]), "+v"(pout[1]), "+v"(pout[2]), "+v"(pout[3]));
   };
   using F = std::integral_constant<bool, false>;
   using T = std::integral_constant<bool, true>;
