@@ -258,8 +258,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ void dma16_raw(u32x4 rsrc, uint32_t voff, uint32_t lds) {
   // One wait state between the scalar write of M0 and its read by the
   // transfer (a GFX9-family hazard).
+  // (lds is wave-uniform; readfirstlane makes that explicit where the
+  // compiler kept it in a vector register)
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc) : "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "m0");
 }
 #pragma clang diagnostic pop
 
@@ -676,6 +678,8 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
 #define SDATTN_FIX_BUFFERS 3
 #endif
 constexpr int kFixBuffers = SDATTN_FIX_BUFFERS;
+template <int V>
+using IntC = std::integral_constant<int, V>;
 
 // LDS layout of the fixed-reference kernel for head dim D (a multiple of 8,
 // DK = D rounded up to 16): rows as short as the operands allow, so that
@@ -898,21 +902,40 @@ void attn_stream_fix(Args16 a) {
   // work -- scores of tile t+1 (into nx), weights of tile t (from cu, into
   // pout) and P.V of tile t-1 (weights pin).  Alternate register roles
   // between consecutive iterations avoid copies.
-  auto body = [&](auto pv_c, auto next_c, auto mask_c, int t, const f32x16 &cu0,
+  // Transfers still allowed in flight at a steady-state barrier (every
+  // iteration in between issues all of its K and V transfers).
+  const int later_ss = __builtin_amdgcn_readfirstlane((NB - 2) * (kc + vc));
+  // PH_c: -1 for the general iteration; else the steady-state form with
+  // t % NB == PH (buffer numbers fold to constants) and t + NB < n (every
+  // transfer is issued, the wait count is later_ss): far fewer scalar
+  // instructions per iteration.
+  auto body = [&](auto pv_c, auto next_c, auto mask_c, auto ph_c, int t, const f32x16 &cu0,
                   const f32x16 &cu1, f32x16 &nx0, f32x16 &nx1, const u32x4 (&pin)[4],
                   u32x4 (&pout)[4]) {
     constexpr bool HAS_PV = decltype(pv_c)::value;
     constexpr bool HAS_NEXT = decltype(next_c)::value;
-    {
+    constexpr int PH = decltype(ph_c)::value;
+    int b, b1, b2, bv;
+    if constexpr (PH >= 0) {
+      vmcnt_barrier_rt<(NB - 2) * P::NIW>(later_ss);
+      b = PH;
+      b1 = (PH + 1) % NB;
+      b2 = (PH + NB - 1) % NB;
+      bv = (PH + NB - 2) % NB;
+      issue_k(t + NB, b);
+      issue_v(t + NB - 2, bv);
+    } else {
       int later = 0;
 #pragma unroll
       for (int j = t + 2 - NB; j < t; ++j) later += issued(j);
       vmcnt_barrier_rt<(NB - 2) * P::NIW>(later);
+      b = t % NB;
+      b1 = b == NB - 1 ? 0 : b + 1;
+      b2 = b == 0 ? NB - 1 : b - 1;
+      bv = b >= 2 ? b - 2 : b + NB - 2;
+      if (t + NB < n) issue_k(t + NB, b);
+      if (t + NB - 2 < n) issue_v(t + NB - 2, bv);
     }
-    const int b = t % NB, b1 = b == NB - 1 ? 0 : b + 1, b2 = b == 0 ? NB - 1 : b - 1;
-    const int bv = b >= 2 ? b - 2 : b + NB - 2;
-    if (t + NB < n) issue_k(t + NB, b);
-    if (t + NB - 2 < n) issue_v(t + NB - 2, bv);
     // The softmax depends on nothing produced in this iteration; an opaque
     // copy of the reference keeps the compiler from hoisting it above the
     // barrier, so it stays in the block it is meant to overlap.
@@ -929,31 +952,44 @@ void attn_stream_fix(Args16 a) {
   };
   using F = std::integral_constant<bool, false>;
   using T = std::integral_constant<bool, true>;
+  using G = std::integral_constant<int, -1>;
 
   u32x4 pA[4], pB[4];
   // Last iteration (no next tile) and the P.V of the last tile.
   auto finish = [&](int t, const f32x16 &cu0, const f32x16 &cu1, const u32x4 (&pin)[4],
                     u32x4 (&pout)[4]) {
-    if (ragged) body(T{}, F{}, T{}, t, cu0, cu1, sA0, sA1, pin, pout);
-    else body(T{}, F{}, F{}, t, cu0, cu1, sA0, sA1, pin, pout);
+    if (ragged) body(T{}, F{}, T{}, G{}, t, cu0, cu1, sA0, sA1, pin, pout);
+    else body(T{}, F{}, F{}, G{}, t, cu0, cu1, sA0, sA1, pin, pout);
     vmcnt_barrier<0>();
     pv(t % NB, pout);
   };
 
   if (n == 1) {
-    if (ragged) body(F{}, F{}, T{}, 0, sA0, sA1, sB0, sB1, pB, pA);
-    else body(F{}, F{}, F{}, 0, sA0, sA1, sB0, sB1, pB, pA);
+    if (ragged) body(F{}, F{}, T{}, G{}, 0, sA0, sA1, sB0, sB1, pB, pA);
+    else body(F{}, F{}, F{}, G{}, 0, sA0, sA1, sB0, sB1, pB, pA);
     vmcnt_barrier<0>();
     pv(0, pA);
   } else {
-    body(F{}, T{}, F{}, 0, sA0, sA1, sB0, sB1, pB, pA);
+    body(F{}, T{}, F{}, G{}, 0, sA0, sA1, sB0, sB1, pB, pA);
     int t = 1;
+    if constexpr (NB == 3) {
+      // Steady state: six iterations run both register roles through all
+      // three buffer phases (t = 1 mod 6 on entry, as t % 3 == 1 and t odd).
+      for (; t + 5 + NB < n; t += 6) {
+        body(T{}, T{}, F{}, IntC<1>{}, t, sB0, sB1, sA0, sA1, pA, pB);
+        body(T{}, T{}, F{}, IntC<2>{}, t + 1, sA0, sA1, sB0, sB1, pB, pA);
+        body(T{}, T{}, F{}, IntC<0>{}, t + 2, sB0, sB1, sA0, sA1, pA, pB);
+        body(T{}, T{}, F{}, IntC<1>{}, t + 3, sA0, sA1, sB0, sB1, pB, pA);
+        body(T{}, T{}, F{}, IntC<2>{}, t + 4, sB0, sB1, sA0, sA1, pA, pB);
+        body(T{}, T{}, F{}, IntC<0>{}, t + 5, sA0, sA1, sB0, sB1, pB, pA);
+      }
+    }
     for (; t + 2 < n; t += 2) {
-      body(T{}, T{}, F{}, t, sB0, sB1, sA0, sA1, pA, pB);
-      body(T{}, T{}, F{}, t + 1, sA0, sA1, sB0, sB1, pB, pA);
+      body(T{}, T{}, F{}, G{}, t, sB0, sB1, sA0, sA1, pA, pB);
+      body(T{}, T{}, F{}, G{}, t + 1, sA0, sA1, sB0, sB1, pB, pA);
     }
     if (t + 1 < n) {
-      body(T{}, T{}, F{}, t, sB0, sB1, sA0, sA1, pA, pB);
+      body(T{}, T{}, F{}, G{}, t, sB0, sB1, sA0, sA1, pA, pB);
       finish(t + 1, sA0, sA1, pB, pA);
     } else {
       finish(t, sB0, sB1, pA, pB);
