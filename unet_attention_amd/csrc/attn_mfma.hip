@@ -941,6 +941,9 @@ void attn_stream_fix(Args16 a) {
     // barrier, so it stays in the block it is meant to overlap.
     float nmt = nm;
     asm volatile("" : "+v"(nmt));
+    // The scheduler's built-in strategy 0 spreads the LDS reads among the
+    // MFMAs of this block (measured 1-3 % faster than its default order).
+    __builtin_amdgcn_iglp_opt(0);
     if constexpr (HAS_NEXT) scores(b1, nx0, nx1);
     weights(mask_c, t * BN, cu0, cu1, nmt, pout);
     if constexpr (HAS_PV) pv(b2, pin);
