@@ -595,10 +595,15 @@ void attn_stream_rescale(Args16 a) {
 // 1.  A key more than ~128 binary orders above it overflows; O or l then ends
 // non-finite, and the wave recomputes its rows with the exact lazily
 // rescaled recurrence, reading K and V straight from memory.
+//
+// fp16 weights have only 16 binary orders of headroom, so in fp16 (H) the
+// kernel also takes each tile's row maximum and, when it exceeds the
+// reference by more than kRescaleSlack, moves the reference up and rescales
+// O: a lazy rescale at tile granularity, inside the same pipeline.
 
 // Exact recurrence for this wave's 32 query rows (32-key sub-tiles, K and V
 // read with buffer loads, no LDS).  Returns the row sum l; O^T in o.
-template <int DK>
+template <int DK, bool H = false>
 __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
                                             const bf16x8 (&qf)[DK / 16], rsrc_t kr,
                                             rsrc_t vr, int Lk, int d, int sl, float c,
@@ -615,7 +620,7 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
       const int c0 = dk * 16 + 8 * h;
       u32x4 x = bload16(kr, (uint32_t)((key0 + r32) * sl + c0) * 2u);
       if (c0 >= d) x = u32x4{0u, 0u, 0u, 0u};
-      sv = mfma32x32x16(as_bf16x8(x), qf[dk], sv);
+      sv = mma<H>(as_bf16x8(x), qf[dk], sv);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -641,8 +646,8 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
         lsum += x;
         p8[j] = x;
       }
-      pk[kk] = u32x4{pack_bf16x2(p8[0], p8[1]), pack_bf16x2(p8[2], p8[3]),
-                     pack_bf16x2(p8[4], p8[5]), pack_bf16x2(p8[6], p8[7])};
+      pk[kk] = u32x4{pack2<H>(p8[0], p8[1]), pack2<H>(p8[2], p8[3]),
+                     pack2<H>(p8[4], p8[5]), pack2<H>(p8[6], p8[7])};
     }
     // V^T operand: lane l supplies column 32*mt + l%32 of V at the keys its
     // weight slots hold (slot j of half h: key 16*kk + 8*(j/4) + 4*h + j%4).
@@ -665,7 +670,7 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
           }
           w[j2] = e[0] | (e[1] << 16);
         }
-        o[mt] = mfma32x32x16(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}),
+        o[mt] = mma<H>(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}),
                              as_bf16x8(pk[kk]), o[mt]);
       }
   }
@@ -714,7 +719,7 @@ struct FixPlan {
   static_assert((KBUF * 2) % 16 == 0 && (VBUF * 2) % 16 == 0, "16-byte aligned buffers");
 };
 
-template <int DK, int D, int NW, bool OUT_F32>
+template <int DK, int D, int NW, bool OUT_F32, bool H = false>
 __global__ __launch_bounds__(NW * kWave, 2)
 void attn_stream_fix(Args16 a) {
   using S = Shape<DK>;
@@ -811,7 +816,7 @@ void attn_stream_fix(Args16 a) {
   }
   if constexpr (S::kOnes) {
     for (int r = tid; r < NB * BN; r += NW * kWave)
-      st16(Vs + r * P::VSTR + D, u32x4{uint32_t(one16<false>()), 0u, 0u, 0u});
+      st16(Vs + r * P::VSTR + D, u32x4{uint32_t(one16<H>()), 0u, 0u, 0u});
   }
 
   const int koff = (lane & 31) * P::KST + 8 * (lane >> 5);
@@ -825,14 +830,13 @@ void attn_stream_fix(Args16 a) {
   // all-ones A operand makes every row of this accumulator sum the bf16
   // weights exactly as P.V uses them.
   f32x16 lacc = {};
-  bf16x8 ones8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones8[i] = (__bf16)1.0f;
+  const uint32_t one2 = uint32_t(one16<H>()) * 0x10001u;
+  const bf16x8 ones8 = as_bf16x8(u32x4{one2, one2, one2, one2});
 
   auto scores = [&](int b, f32x16 &s0, f32x16 &s1) {
     const uint16_t *kb = Ks + b * P::KBUF + koff;
-    s0 = scores_subtile<DK>(kb, qf);
-    s1 = scores_subtile<DK>(kb + 32 * P::KST, qf);
+    s0 = scores_subtile<DK, H>(kb, qf);
+    s1 = scores_subtile<DK, H>(kb + 32 * P::KST, qf);
   };
   auto pv = [&](int b, const u32x4 (&pk)[4]) {
     const uint16_t *vb = Vs + b * P::VBUF + voff;
@@ -844,9 +848,9 @@ void attn_stream_fix(Args16 a) {
         const s16x4 lo = ld_tr16(vp), hi = ld_tr16(vp + 8 * P::VSTR);
         const bf16x8 av =
             __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mt] = mfma32x32x16(av, as_bf16x8(pk[kc4]), o[mt]);
+        o[mt] = mma<H>(av, as_bf16x8(pk[kc4]), o[mt]);
         if constexpr (!S::kOnes)
-          if (mt == 0) lacc = mfma32x32x16(ones8, as_bf16x8(pk[kc4]), lacc);
+          if (mt == 0) lacc = mma<H>(ones8, as_bf16x8(pk[kc4]), lacc);
       }
   };
 
@@ -891,8 +895,8 @@ void attn_stream_fix(Args16 a) {
           }
           p8[j] = x;
         }
-        pk[2 * u + kk] = u32x4{pack_bf16x2(p8[0], p8[1]), pack_bf16x2(p8[2], p8[3]),
-                               pack_bf16x2(p8[4], p8[5]), pack_bf16x2(p8[6], p8[7])};
+        pk[2 * u + kk] = u32x4{pack2<H>(p8[0], p8[1]), pack2<H>(p8[2], p8[3]),
+                               pack2<H>(p8[4], p8[5]), pack2<H>(p8[6], p8[7])};
       }
   };
 
@@ -936,6 +940,29 @@ void attn_stream_fix(Args16 a) {
       if (t + NB < n) issue_k(t + NB, b);
       if (t + NB - 2 < n) issue_v(t + NB - 2, bv);
     }
+    // fp16 weights must stay below fp16's largest value: when a row's tile
+    // maximum rises more than kRescaleSlack above the reference, the
+    // reference moves up.  O still receives tile t-1's weights (taken against
+    // the old reference) in this block, so it is scaled after that P.V.
+    float alpha = 1.f;
+    bool resc = false;
+    if constexpr (H) {
+      f32x16 m0 = cu0, m1 = cu1;
+      if constexpr (decltype(mask_c)::value) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (t * BN + acc_key(i, lane) >= Lk) m0[i] = -__builtin_inff();
+          if (t * BN + 32 + acc_key(i, lane) >= Lk) m1[i] = -__builtin_inff();
+        }
+      }
+      const float tmax = max_halves(max16(m1, max16(m0, -__builtin_inff()))) * c;
+      if (__any(tmax + nm > kRescaleSlack)) {
+        const float mref = fmaxf(-nm, tmax);
+        alpha = fast_exp2(-nm - mref);
+        nm = -mref;
+        resc = true;
+      }
+    }
     // The softmax depends on nothing produced in this iteration; an opaque
     // copy of the reference keeps the compiler from hoisting it above the
     // barrier, so it stays in the block it is meant to overlap.
@@ -947,6 +974,14 @@ void attn_stream_fix(Args16 a) {
     if constexpr (HAS_NEXT) scores(b1, nx0, nx1);
     weights(mask_c, t * BN, cu0, cu1, nmt, pout);
     if constexpr (HAS_PV) pv(b2, pin);
+    if constexpr (H) {
+      if (resc) {
+        asm volatile("");  // a real branch: if-converted, it would scale O every tile
+#pragma unroll
+        for (int mt = 0; mt < S::MT; ++mt) o[mt] *= alpha;
+        if constexpr (!S::kOnes) lacc *= alpha;
+      }
+    }
     // The weights are consumed only in the next iteration.  This opaque use
     // keeps the compiler from sinking their computation below the next
     // barrier: it did so in every other iteration, leaving one block with
@@ -1020,9 +1055,9 @@ void attn_stream_fix(Args16 a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (mt * 32 + 8 * (i >> 2) + hb + (i & 3) < D) ok = ok && __builtin_isfinite(o[mt][i]);
-  if (__any(!ok)) l = rows_exact<DK>(o, qf, kr, vr, Lk, d, slk, c, lane);
+  if (__any(!ok)) l = rows_exact<DK, H>(o, qf, kr, vr, Lk, d, slk, c, lane);
 
-  store_out_l<DK, OUT_F32>(o, l, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
+  store_out_l<DK, OUT_F32, H>(o, l, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1287,7 +1322,7 @@ void launch_rescale(Args16 a, int BH, bool out_f32, hipStream_t stream) {
                        0, stream, a);
 }
 
-template <int DK>
+template <int DK, bool H>
 void launch_fix(Args16 a, int BH, bool out_f32, hipStream_t stream) {
   constexpr int NW = kStreamFixWaves;
   a.qblocks = (a.Lq + NW * kQW - 1) / (NW * kQW);
@@ -1295,37 +1330,38 @@ void launch_fix(Args16 a, int BH, bool out_f32, hipStream_t stream) {
   // d is DK or DK - 8 (d % 8 == 0); each has its own LDS layout.
   if (a.d == DK) {
     if (out_f32)
-      hipLaunchKernelGGL((attn_stream_fix<DK, DK, NW, true>), dim3(a.nwg), dim3(NW * kWave), 0,
+      hipLaunchKernelGGL((attn_stream_fix<DK, DK, NW, true, H>), dim3(a.nwg), dim3(NW * kWave), 0,
                          stream, a);
     else
-      hipLaunchKernelGGL((attn_stream_fix<DK, DK, NW, false>), dim3(a.nwg), dim3(NW * kWave),
+      hipLaunchKernelGGL((attn_stream_fix<DK, DK, NW, false, H>), dim3(a.nwg), dim3(NW * kWave),
                          0, stream, a);
   } else {
     if (out_f32)
-      hipLaunchKernelGGL((attn_stream_fix<DK, DK - 8, NW, true>), dim3(a.nwg),
+      hipLaunchKernelGGL((attn_stream_fix<DK, DK - 8, NW, true, H>), dim3(a.nwg),
                          dim3(NW * kWave), 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_stream_fix<DK, DK - 8, NW, false>), dim3(a.nwg),
+      hipLaunchKernelGGL((attn_stream_fix<DK, DK - 8, NW, false, H>), dim3(a.nwg),
                          dim3(NW * kWave), 0, stream, a);
   }
 }
 
-// bf16: short-key kernel, else the fixed-reference kernel up to DK 64 and
-// the rescaling kernel above.  fp16 weights would overflow fp16's range
-// under a fixed reference, so fp16 streams through the rescaling kernel
-// (weights <= 2^8) at every head dim.
+// Short-key kernel up to the key cap, else the fixed-reference kernel up to
+// DK 64 and the rescaling kernel above.  In fp16 the fixed-reference kernel
+// moves its reference up whenever a tile would push weights past 2^8 (fp16's
+// range ends at 65504); bf16 weights share fp32's exponent range and never
+// need that.
 template <int DK>
 hipError_t launch_dk(const Args16 &a, int BH, bool short_path, bool out_f32, bool half,
                      hipStream_t stream) {
-  if (half) {
-    if (short_path) launch_short<DK, true>(a, BH, out_f32, stream);
-    else launch_rescale<DK, true>(a, BH, out_f32, stream);
-  } else if (short_path) {
-    launch_short<DK, false>(a, BH, out_f32, stream);
+  if (short_path) {
+    if (half) launch_short<DK, true>(a, BH, out_f32, stream);
+    else launch_short<DK, false>(a, BH, out_f32, stream);
   } else if constexpr (DK <= kStreamFixMaxDk) {
-    launch_fix<DK>(a, BH, out_f32, stream);
+    if (half) launch_fix<DK, true>(a, BH, out_f32, stream);
+    else launch_fix<DK, false>(a, BH, out_f32, stream);
   } else {
-    launch_rescale<DK, false>(a, BH, out_f32, stream);
+    if (half) launch_rescale<DK, true>(a, BH, out_f32, stream);
+    else launch_rescale<DK, false>(a, BH, out_f32, stream);
   }
   return hipGetLastError();
 }
