@@ -1205,6 +1205,9 @@ void attn_short(Args16 a) {
       if (nt < nkt) {
         s[nt] = scores_subtile<DK, H>(Ks + koff + nt * 32 * S::KST, qf);
         if (nt == nkt - 1) {
+          // A real (uniform) branch: if-converted, the masking would run on
+          // every sub-tile.
+          asm volatile("");
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (nt * 32 + acc_key(i, lane) >= Lk) s[nt][i] = -__builtin_inff();
@@ -1228,12 +1231,18 @@ void attn_short(Args16 a) {
           if (kk == 1 && nt * 32 + 16 >= Lk) break;  // chunk entirely past Lk
           float p[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 8 * kk + j;
-            float x = fast_exp2(__builtin_fmaf(s[nt][i], c, nm));
-            if (last && nt * 32 + acc_key(i, lane) >= Lk) x = 0.f;
-            p[j] = x;
-            if constexpr (!S::kOnes) lsum += x;
+          for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(s[nt][8 * kk + j], c, nm));
+          if (last) {
+            // masked scores are -inf, so these weights are already 0 unless
+            // the scale is 0 (-inf * 0); zero them explicitly
+            asm volatile("");
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (nt * 32 + acc_key(8 * kk + j, lane) >= Lk) p[j] = 0.f;
+          }
+          if constexpr (!S::kOnes) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) lsum += p[j];
           }
           const u32x4 pk = {pack2<H>(p[0], p[1]), pack2<H>(p[2], p[3]),
                             pack2<H>(p[4], p[5]), pack2<H>(p[6], p[7])};
