@@ -716,6 +716,9 @@ struct FixPlan {
   static constexpr int VI = (BN * VCR + 63) / 64;
   static constexpr int NI = KI + VI;
   static constexpr int NIW = (NI + NW - 1) / NW;
+  // K rows without padding (KST == D) fill whole 64-lane transfers: every
+  // lane of every K transfer is active.
+  static constexpr bool KFULL = KST == D && (BN * KCR) % 64 == 0;
   static_assert((KBUF * 2) % 16 == 0 && (VBUF * 2) % 16 == 0, "16-byte aligned buffers");
 };
 
@@ -783,8 +786,10 @@ void attn_stream_fix(Args16 a) {
     const uint32_t dst = ks_lds + (uint32_t)(b * P::KBUF) * 2u;
 #pragma unroll
     for (int r = 0; r < P::NIW; ++r)
-      if (wave + NW * r < P::NI && isk[r])
-        if (act[r]) dma16_raw(kw, toff + goff[r], dst + loff[r]);
+      if (wave + NW * r < P::NI && isk[r]) {
+        if constexpr (P::KFULL) dma16_raw(kw, toff + goff[r], dst + loff[r]);
+        else if (act[r]) dma16_raw(kw, toff + goff[r], dst + loff[r]);
+      }
   };
   auto issue_v = [&](int tt, int b) {
     const uint32_t toff = (uint32_t)(tt * BN * slk) * 2u;
