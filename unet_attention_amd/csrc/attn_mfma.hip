@@ -258,10 +258,8 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ void dma16_raw(u32x4 rsrc, uint32_t voff, uint32_t lds) {
   // One wait state between the scalar write of M0 and its read by the
   // transfer (a GFX9-family hazard).
-  // (lds is wave-uniform; readfirstlane makes that explicit where the
-  // compiler kept it in a vector register)
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "m0");
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "m0");
 }
 #pragma clang diagnostic pop
 
@@ -787,8 +785,11 @@ void attn_stream_fix(Args16 a) {
 #pragma unroll
     for (int r = 0; r < P::NIW; ++r)
       if (wave + NW * r < P::NI && isk[r]) {
-        if constexpr (P::KFULL) dma16_raw(kw, toff + goff[r], dst + loff[r]);
-        else if (act[r]) dma16_raw(kw, toff + goff[r], dst + loff[r]);
+        // wave-uniform; readfirstlane keeps it in a scalar register where
+        // the compiler would otherwise leave it in a vector one
+        const uint32_t l = __builtin_amdgcn_readfirstlane(dst + loff[r]);
+        if constexpr (P::KFULL) dma16_raw(kw, toff + goff[r], l);
+        else if (act[r]) dma16_raw(kw, toff + goff[r], l);
       }
   };
   auto issue_v = [&](int tt, int b) {
@@ -796,8 +797,10 @@ void attn_stream_fix(Args16 a) {
     const uint32_t dst = vs_lds + (uint32_t)(b * P::VBUF) * 2u;
 #pragma unroll
     for (int r = 0; r < P::NIW; ++r)
-      if (wave + NW * r < P::NI && !isk[r])
-        if (act[r]) dma16_raw(vw, toff + goff[r], dst + loff[r]);
+      if (wave + NW * r < P::NI && !isk[r]) {
+        const uint32_t l = __builtin_amdgcn_readfirstlane(dst + loff[r]);
+        if (act[r]) dma16_raw(vw, toff + goff[r], l);
+      }
   };
 
   // Transfers this wave issues in iteration j (prologue included).
