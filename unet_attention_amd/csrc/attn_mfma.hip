@@ -1297,6 +1297,11 @@ constexpr int kStreamWaves = SDATTN_STREAM_WAVES;          // rescaling streamin
 constexpr int kSplitBelow = SDATTN_SPLIT_BELOW;
 constexpr int kShortWaves = SDATTN_SHORT_WAVES;
 constexpr int kShortTiles = SDATTN_SHORT_TILES;   // query tiles per wave (short kernel)
+// Below this many four-wave workgroups the short kernel runs two-wave ones.
+#ifndef SDATTN_SHORT_NARROW_BELOW
+#define SDATTN_SHORT_NARROW_BELOW 64
+#endif
+constexpr int kShortNarrowBelow = SDATTN_SHORT_NARROW_BELOW;
 
 template <int DK, bool H>
 void launch_short(Args16 a, int BH, bool out_f32, hipStream_t stream) {
@@ -1304,6 +1309,22 @@ void launch_short(Args16 a, int BH, bool out_f32, hipStream_t stream) {
   const int per_wg = NW * kQW * QPW;
   a.qblocks = (a.Lq + per_wg - 1) / per_wg;
   a.nwg = BH * a.qblocks;
+  if constexpr (NW == 4 && QPW == 1) {
+    if (a.nwg < kShortNarrowBelow) {
+      // few workgroups (the 16x16 level): two-wave workgroups spread the
+      // same waves over twice as many CUs
+      constexpr int NW2 = 2;
+      a.qblocks = (a.Lq + NW2 * kQW - 1) / (NW2 * kQW);
+      a.nwg = BH * a.qblocks;
+      if (out_f32)
+        hipLaunchKernelGGL((attn_short<DK, NW2, 1, KMAX, true, H>), dim3(a.nwg),
+                           dim3(NW2 * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_short<DK, NW2, 1, KMAX, false, H>), dim3(a.nwg),
+                           dim3(NW2 * kWave), 0, stream, a);
+      return;
+    }
+  }
   if (out_f32)
     hipLaunchKernelGGL((attn_short<DK, NW, QPW, KMAX, true, H>), dim3(a.nwg), dim3(NW * kWave),
                        0, stream, a);
