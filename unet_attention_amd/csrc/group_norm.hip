@@ -30,6 +30,9 @@ namespace {
 constexpr int kGnThreads = 512;                      // 8 waves
 constexpr int kGnWaves = kGnThreads / kWave;
 constexpr int kMaxChunksPerThread = 16;               // 8 elements per chunk
+// Chunks of its own slice a split-form workgroup keeps in registers per
+// thread (a larger slice is read again for the normalisation).
+constexpr int kSliceChunks = 10;
 constexpr int kMaxResident = kGnThreads * kMaxChunksPerThread * 8;  // 65536
 constexpr int kMaxGroupChannels = 8192;  // gamma + beta of a group in <= 64 KB of LDS
 
@@ -132,11 +135,12 @@ __device__ __forceinline__ void normalise_store(const GnArgs &a, size_t e, const
 }
 
 // Shifted sums s1 += x - x0, s2 += (x - x0)^2 over this thread's chunks
-// tid, tid + kGnThreads, ... of [0, nch), U chunk loads in flight at a time.
+// ja + tid, ja + tid + kGnThreads, ... of [ja, nch), U chunk loads in flight
+// at a time.
 template <int ET, int U>
-__device__ __forceinline__ void shifted_sums(const void *x, size_t base, int nch, float x0,
-                                             float &s1, float &s2) {
-  for (int j0 = threadIdx.x; j0 < nch; j0 += U * kGnThreads) {
+__device__ __forceinline__ void shifted_sums(const void *x, size_t base, int ja, int nch,
+                                             float x0, float &s1, float &s2) {
+  for (int j0 = ja + (int)threadIdx.x; j0 < nch; j0 += U * kGnThreads) {
     float v[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(kGnThreads) void group_norm_stream(GnArgs a) {
   load8<ET>(a.x, base, first);
   const float x0 = first[0];
   float s1 = 0.f, s2 = 0.f;
-  shifted_sums<ET, 8>(a.x, base, nch, x0, s1, s2);
+  shifted_sums<ET, 8>(a.x, base, 0, nch, x0, s1, s2);
   const float m = (float)nch * 8.0f;
   const float S1 = block_sum(s1, red);
   const float S2 = block_sum(s2, red);
@@ -291,18 +295,56 @@ __global__ __launch_bounds__(kGnThreads) void group_norm_split(GnArgs a) {
   float first[8];
   load8<ET>(a.x, base, first);
   const float x0 = first[0];
-  float s1 = 0.f, s2 = 0.f;
-  shifted_sums<ET, 8>(a.x, base, nch, x0, s1, s2);
+  const int j0 = (int)((long long)k * nch / K), j1 = (int)((long long)(k + 1) * nch / K);
   const float m = (float)nch * 8.0f;
+  if (j1 - j0 <= kSliceChunks * kGnThreads) {
+    // This workgroup's slice stays in registers from the statistics pass to
+    // the normalisation (read once; its loads overlap the rest of the group).
+    const int cpc = a.S / 8;
+    float own[kSliceChunks][8];
+#pragma unroll
+    for (int u = 0; u < kSliceChunks; ++u) {
+      const int j = j0 + tid + u * kGnThreads;
+      if (j < j1) load8<ET>(a.x, base + (size_t)j * 8, own[u]);
+    }
+    float s1 = 0.f, s2 = 0.f;
+    shifted_sums<ET, 8>(a.x, base, 0, j0, x0, s1, s2);
+    shifted_sums<ET, 8>(a.x, base, j1, nch, x0, s1, s2);
+#pragma unroll
+    for (int u = 0; u < kSliceChunks; ++u) {
+      if (j0 + tid + u * kGnThreads < j1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float t = own[u][i] - x0;
+          s1 += t;
+          s2 = __builtin_fmaf(t, t, s2);
+        }
+      }
+    }
+    const float S1 = block_sum(s1, red);
+    const float S2 = block_sum(s2, red);
+    const float d1 = S1 / m;
+    const float mu = x0 + d1;
+    const float var = fmaxf(S2 / m - d1 * d1, 0.f);
+    const float rstd = 1.0f / sqrtf(var + a.eps);
+#pragma unroll
+    for (int u = 0; u < kSliceChunks; ++u) {
+      const int j = j0 + tid + u * kGnThreads;
+      if (j < j1)
+        normalise_store<ET, OUT_F32, SILU>(a, base + (size_t)j * 8, gb, cpg, j / cpc, mu, rstd,
+                                           own[u]);
+    }
+    return;
+  }
+  float s1 = 0.f, s2 = 0.f;
+  shifted_sums<ET, 8>(a.x, base, 0, nch, x0, s1, s2);
   const float S1 = block_sum(s1, red);
   const float S2 = block_sum(s2, red);
   const float d1 = S1 / m;
   const float mu = x0 + d1;
   const float var = fmaxf(S2 / m - d1 * d1, 0.f);
   const float rstd = 1.0f / sqrtf(var + a.eps);
-  normalise_range<ET, OUT_F32, SILU, 4>(a, base, (int)((long long)k * nch / K),
-                                        (int)((long long)(k + 1) * nch / K), gb, cpg, mu, rstd);
-  (void)tid;
+  normalise_range<ET, OUT_F32, SILU, 4>(a, base, j0, j1, gb, cpg, mu, rstd);
 }
 
 template <int ET, bool OUT_F32, bool SILU>
