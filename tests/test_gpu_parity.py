@@ -243,21 +243,28 @@ def test_negative_scale_and_dominant_key(dev, entry):
     assert np.abs(got - want2).max() <= 1e-5
 
 
-def test_shifted_keys_stress_running_max(dev):
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [40, 64])
+def test_shifted_keys_stress_running_max(dev, d, dtype):
     """Keys shifted by a large common vector: scores reach |s| ~ 40 with a
-    running maximum that keeps growing; compare with the oracle on the same
-    (rounded) inputs."""
+    maximum that keeps growing along the keys (in fp16 the streaming kernel
+    must move its reference up many times); compare with the oracle on the
+    same (rounded) inputs."""
     import torch
     from workloads import bf16_bits_to_f32, round_to_bf16_bits
-    d, Lk = 64, 1500
+    Lk = 1500
     q = _rand((1, 2, 96, d), 11)
     k = _rand((1, 2, Lk, d), 12) + np.linspace(0, 6, Lk, dtype=np.float32)[None, None, :, None]
     v = _rand((1, 2, Lk, d), 13)
-    q, k, v = (bf16_bits_to_f32(round_to_bf16_bits(a)) for a in (q, k, v))
+    if dtype == "f16":
+        q, k, v = (a.astype(np.float16).astype(np.float32) for a in (q, k, v))
+    else:
+        q, k, v = (bf16_bits_to_f32(round_to_bf16_bits(a)) for a in (q, k, v))
     want = oracle.attn(q, k, v, 0.125)
-    tq, tk, tv = tensors_from_f32(q, k, v, "bf16")
-    say("shifted keys")
-    assert_bf16_gate(run("auto", tq, tk, tv, 0.125, torch.float32), want, "shifted keys")
+    tq, tk, tv = tensors_from_f32(q, k, v, dtype)
+    say(f"shifted keys d={d} {dtype}")
+    assert_bf16_gate(run("auto", tq, tk, tv, 0.125, torch.float32), want,
+                     f"shifted keys d={d} {dtype}")
 
 
 def _aligned_key_case(d, seed, v_big=None, dtype="bf16"):
