@@ -1,0 +1,69 @@
+"""Seeded random shapes through every attention entry point, against the fp64
+oracle.  The hand-picked parity cases pin the workloads and the edge cases;
+this sweep reaches the combinations in between (head dims 8..256, ragged
+query and key lengths, batch x head counts that put the streaming kernels in
+their plain or split grid forms, bf16 / fp16 / fp32, every output type).
+Case i draws everything from numpy's PCG64 seeded with 20000 + i, so a
+failure names a reproducible case.  Needs a GPU; marked ``gpu``.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import (assert_bf16_gate, assert_bf16_out_gate, assert_f32_gate, run,
+                            say, to_device)
+from workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 64
+
+
+def _case(i):
+    r = np.random.default_rng(20000 + i)
+    dtype = ("bf16", "bf16", "f16", "f32")[int(r.integers(4))]
+    # half the cases at d <= 64 (the fixed-reference kernel), half above
+    d = int(r.integers(1, 9)) * 8 if r.random() < 0.5 else int(r.integers(9, 33)) * 8
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
+    Lq = int(r.integers(1, 700))
+    Lk = int(r.choice([int(r.integers(1, 129)), int(r.integers(129, 1100))]))
+    scale = float(np.float32(d ** -0.5 * r.choice([0.5, 1.0, 2.0])))
+    return Workload(f"rand{i}", "self", B, H, Lq, Lk, d, dtype, 20000 + i), scale
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import unet_attention_amd as sd
+    sd.load()
+    return "cuda"
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape(dev, i):
+    import torch
+    import unet_attention_amd as sd
+    w, scale = _case(i)
+    x = make_inputs(w)
+    want = oracle.attn(x.q, x.k, x.v, scale)
+    q, k, v = to_device(x)
+    what = f"case {i}: {w.dtype} B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} d{w.d} scale {scale:.4g}"
+    if w.dtype == "f32":
+        say(what)
+        assert_f32_gate(run("auto", q, k, v, scale), want, what)
+        return
+    code = sd.SDATTN_DTYPE_BF16 if w.dtype == "bf16" else sd.SDATTN_DTYPE_F16
+    entries = ["auto", "stream"]
+    if w.Lk <= sd.sdattn_cross_max_ctx(w.d, code):
+        entries.append("cross")
+    t16 = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    for entry in entries:
+        say(f"{what} entry={entry}")
+        assert_bf16_gate(run(entry, q, k, v, scale, out_dtype=torch.float32), want,
+                         f"{what} {entry}")
+        assert_bf16_out_gate(run(entry, q, k, v, scale, out_dtype=t16), want,
+                             f"{what} {entry} 16-bit out", out=w.dtype)
