@@ -67,3 +67,30 @@ def test_random_shape(dev, i):
                          f"{what} {entry}")
         assert_bf16_out_gate(run(entry, q, k, v, scale, out_dtype=t16), want,
                              f"{what} {entry} 16-bit out", out=w.dtype)
+
+
+@pytest.mark.parametrize("i", range(0, N_CASES, 4))
+def test_random_shape_token_major(dev, i):
+    """The same random cases (every fourth) with token-major [B, L, H*d]
+    operands cut from a fused [B, L, 3*H*d] projection (row stride 3C): the
+    result must equal the head-major entry's bit for bit."""
+    import torch
+    import unet_attention_amd as sd
+    w, scale = _case(i)
+    x = make_inputs(w)
+    q, k, v = to_device(x)
+    B, H, d = w.B, w.H, w.d
+    odt = torch.float32
+    ref = sd.fwd(q, k, v, scale=scale, out_dtype=odt)
+    C = H * d
+    fused_q = torch.zeros((B, w.Lq, 3 * C), dtype=q.dtype, device=dev)
+    fused_kv = torch.zeros((B, w.Lk, 3 * C), dtype=q.dtype, device=dev)
+    fused_q[:, :, :C] = q.permute(0, 2, 1, 3).reshape(B, w.Lq, C)
+    fused_kv[:, :, C:2 * C] = k.permute(0, 2, 1, 3).reshape(B, w.Lk, C)
+    fused_kv[:, :, 2 * C:] = v.permute(0, 2, 1, 3).reshape(B, w.Lk, C)
+    say(f"token-major case {i}: {w.dtype} B{B} H{H} Lq{w.Lq} Lk{w.Lk} d{d}")
+    got = sd.fwd_tokens(fused_q[:, :, :C], fused_kv[:, :, C:2 * C], fused_kv[:, :, 2 * C:], H,
+                        scale=scale, out_dtype=odt)
+    torch.cuda.synchronize()
+    got_hm = got.view(B, w.Lq, H, d).permute(0, 2, 1, 3)
+    assert torch.equal(got_hm, ref), f"case {i}: token-major result differs from head-major"
