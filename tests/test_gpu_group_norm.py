@@ -125,3 +125,34 @@ def test_group_norm_constant_groups_give_beta(dev):
     torch.cuda.synchronize()
     err = (y - beta[None, :, None]).abs().max().item()
     assert err <= 1e-5, f"constant groups: {err:.3e}"
+
+
+def _gn_case(i):
+    """Seeded random GroupNorm problem: every kernel form (register-resident,
+    streaming, split), all element types, SiLU on or off, in place or not."""
+    from workloads import GnWorkload
+    r = np.random.default_rng(30000 + i)
+    G = int(r.choice([1, 2, 4, 8, 16, 32]))
+    C = G * int(r.integers(1, 21))
+    H = int(r.integers(1, 65))
+    W = 8 * int(r.integers(1, 17))
+    N = int(r.integers(1, 4))
+    dtype = ("bf16", "f16", "f32")[int(r.integers(3))]
+    w = GnWorkload(f"gnrand{i}", N, C, H, W, G, dtype, 30000 + i,
+                   eps=float(r.choice([1e-5, 1e-6])), silu=bool(r.integers(2)))
+    return w, bool(r.integers(2))
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_group_norm_random(dev, i):
+    import torch
+    w, in_place = _gn_case(i)
+    x = make_gn_inputs(w)
+    want = oracle.group_norm(x.x, x.gamma, x.beta, w.G, w.eps, w.silu).astype(np.float64)
+    say(f"group norm random {i}: {w} in_place={in_place}")
+    if in_place:
+        y = _run(w, x, dev, out=_device_x(x, dev))
+        _check(y.float().cpu().numpy().astype(np.float64), want, w.dtype, f"random {i} in place")
+    else:
+        y = _run(w, x, dev, out_dtype=torch.float32)
+        _check(y.cpu().numpy().astype(np.float64), want, "f32", f"random {i}")
