@@ -81,11 +81,12 @@ def test_group_norm_workloads(dev, name, dtype, silu):
 
 
 @pytest.mark.parametrize("N,C,H,W,G", [(3, 12, 4, 6, 4), (1, 8, 8, 1, 8), (2, 64, 2, 4, 1),
-                                       (1, 4, 128, 136, 2)])
+                                       (1, 4, 128, 136, 2), (1, 32, 128, 128, 1)])
 def test_group_norm_odd_shapes(dev, N, C, H, W, G):
     """Groups of one channel, one group over all channels, chunk counts that
-    do not fill the workgroup, and a 34816-element group (register path
-    near its widest tile count)."""
+    do not fill the workgroup, a 34816-element group (register path near its
+    widest tile count), and a 524288-element group whose split slices are
+    too large to stay in registers."""
     from workloads import GnWorkload
     w = GnWorkload("odd", N, C, H, W, G, "bf16", 7100 + N * C + H * W + G)
     x = make_gn_inputs(w)
