@@ -127,13 +127,12 @@ hipError_t launch_f32(const F32Args &base, int BH, hipStream_t stream) {
   a.qblocks = (a.Lq + kQB - 1) / kQB;
   const dim3 grid(BH * a.qblocks), block(kWave);
   switch ((a.d + kWave - 1) / kWave) {
-    case 1: hipLaunchKernelGGL(attn_f32_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(attn_f32_kernel<2>, grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(attn_f32_kernel<3>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(attn_f32_kernel<4>, grid, block, 0, stream, a); break;
+    case 1: return launch_kernel(&attn_f32_kernel<1>, grid, block, 0, stream, a);
+    case 2: return launch_kernel(&attn_f32_kernel<2>, grid, block, 0, stream, a);
+    case 3: return launch_kernel(&attn_f32_kernel<3>, grid, block, 0, stream, a);
+    case 4: return launch_kernel(&attn_f32_kernel<4>, grid, block, 0, stream, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace sdattn

@@ -1304,7 +1304,7 @@ constexpr int kShortTiles = SDATTN_SHORT_TILES;   // query tiles per wave (short
 constexpr int kShortNarrowBelow = SDATTN_SHORT_NARROW_BELOW;
 
 template <int DK, bool H>
-void launch_short(Args16 a, int BH, bool out_f32, hipStream_t stream) {
+hipError_t launch_short(Args16 a, int BH, bool out_f32, hipStream_t stream) {
   constexpr int NW = kShortWaves, QPW = kShortTiles, KMAX = short_cap<DK>();
   const int per_wg = NW * kQW * QPW;
   a.qblocks = (a.Lq + per_wg - 1) / per_wg;
@@ -1316,71 +1316,52 @@ void launch_short(Args16 a, int BH, bool out_f32, hipStream_t stream) {
       constexpr int NW2 = 2;
       a.qblocks = (a.Lq + NW2 * kQW - 1) / (NW2 * kQW);
       a.nwg = BH * a.qblocks;
-      if (out_f32)
-        hipLaunchKernelGGL((attn_short<DK, NW2, 1, KMAX, true, H>), dim3(a.nwg),
-                           dim3(NW2 * kWave), 0, stream, a);
-      else
-        hipLaunchKernelGGL((attn_short<DK, NW2, 1, KMAX, false, H>), dim3(a.nwg),
-                           dim3(NW2 * kWave), 0, stream, a);
-      return;
+      const dim3 grid(a.nwg), block(NW2 * kWave);
+      return out_f32
+                 ? launch_kernel(&attn_short<DK, NW2, 1, KMAX, true, H>, grid, block, 0, stream, a)
+                 : launch_kernel(&attn_short<DK, NW2, 1, KMAX, false, H>, grid, block, 0, stream, a);
     }
   }
-  if (out_f32)
-    hipLaunchKernelGGL((attn_short<DK, NW, QPW, KMAX, true, H>), dim3(a.nwg), dim3(NW * kWave),
-                       0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_short<DK, NW, QPW, KMAX, false, H>), dim3(a.nwg),
-                       dim3(NW * kWave), 0, stream, a);
+  const dim3 grid(a.nwg), block(NW * kWave);
+  return out_f32 ? launch_kernel(&attn_short<DK, NW, QPW, KMAX, true, H>, grid, block, 0, stream, a)
+                 : launch_kernel(&attn_short<DK, NW, QPW, KMAX, false, H>, grid, block, 0, stream, a);
 }
 
 template <int DK, bool H>
-void launch_rescale(Args16 a, int BH, bool out_f32, hipStream_t stream) {
+hipError_t launch_rescale(Args16 a, int BH, bool out_f32, hipStream_t stream) {
   constexpr int NW = kStreamWaves;
   a.qblocks = (a.Lq + NW * kQW - 1) / (NW * kQW);
   a.nwg = BH * a.qblocks;
+  const dim3 block(NW * kWave);
   if constexpr (DmaPlan<DK, NW>::NSUB == 2) {
     if (a.nwg < kSplitBelow) {
       // few workgroups for the chip: two waves share each query block
       a.qblocks = (a.Lq + NW / 2 * kQW - 1) / (NW / 2 * kQW);
       a.nwg = BH * a.qblocks;
-      if (out_f32)
-        hipLaunchKernelGGL((attn_stream_rescale<DK, NW, true, H, 2>), dim3(a.nwg),
-                           dim3(NW * kWave), 0, stream, a);
-      else
-        hipLaunchKernelGGL((attn_stream_rescale<DK, NW, false, H, 2>), dim3(a.nwg),
-                           dim3(NW * kWave), 0, stream, a);
-      return;
+      const dim3 grid(a.nwg);
+      return out_f32
+                 ? launch_kernel(&attn_stream_rescale<DK, NW, true, H, 2>, grid, block, 0, stream, a)
+                 : launch_kernel(&attn_stream_rescale<DK, NW, false, H, 2>, grid, block, 0, stream, a);
     }
   }
-  if (out_f32)
-    hipLaunchKernelGGL((attn_stream_rescale<DK, NW, true, H>), dim3(a.nwg), dim3(NW * kWave), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((attn_stream_rescale<DK, NW, false, H>), dim3(a.nwg), dim3(NW * kWave),
-                       0, stream, a);
+  const dim3 grid(a.nwg);
+  return out_f32 ? launch_kernel(&attn_stream_rescale<DK, NW, true, H>, grid, block, 0, stream, a)
+                 : launch_kernel(&attn_stream_rescale<DK, NW, false, H>, grid, block, 0, stream, a);
 }
 
 template <int DK, bool H>
-void launch_fix(Args16 a, int BH, bool out_f32, hipStream_t stream) {
+hipError_t launch_fix(Args16 a, int BH, bool out_f32, hipStream_t stream) {
   constexpr int NW = kStreamFixWaves;
   a.qblocks = (a.Lq + NW * kQW - 1) / (NW * kQW);
   a.nwg = BH * a.qblocks;
+  const dim3 grid(a.nwg), block(NW * kWave);
   // d is DK or DK - 8 (d % 8 == 0); each has its own LDS layout.
-  if (a.d == DK) {
-    if (out_f32)
-      hipLaunchKernelGGL((attn_stream_fix<DK, DK, NW, true, H>), dim3(a.nwg), dim3(NW * kWave), 0,
-                         stream, a);
-    else
-      hipLaunchKernelGGL((attn_stream_fix<DK, DK, NW, false, H>), dim3(a.nwg), dim3(NW * kWave),
-                         0, stream, a);
-  } else {
-    if (out_f32)
-      hipLaunchKernelGGL((attn_stream_fix<DK, DK - 8, NW, true, H>), dim3(a.nwg),
-                         dim3(NW * kWave), 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_stream_fix<DK, DK - 8, NW, false, H>), dim3(a.nwg),
-                         dim3(NW * kWave), 0, stream, a);
-  }
+  if (a.d == DK)
+    return out_f32 ? launch_kernel(&attn_stream_fix<DK, DK, NW, true, H>, grid, block, 0, stream, a)
+                   : launch_kernel(&attn_stream_fix<DK, DK, NW, false, H>, grid, block, 0, stream, a);
+  return out_f32
+             ? launch_kernel(&attn_stream_fix<DK, DK - 8, NW, true, H>, grid, block, 0, stream, a)
+             : launch_kernel(&attn_stream_fix<DK, DK - 8, NW, false, H>, grid, block, 0, stream, a);
 }
 
 // Short-key kernel up to the key cap, else the fixed-reference kernel up to
@@ -1391,21 +1372,48 @@ void launch_fix(Args16 a, int BH, bool out_f32, hipStream_t stream) {
 template <int DK>
 hipError_t launch_dk(const Args16 &a, int BH, bool short_path, bool out_f32, bool half,
                      hipStream_t stream) {
-  if (short_path) {
-    if (half) launch_short<DK, true>(a, BH, out_f32, stream);
-    else launch_short<DK, false>(a, BH, out_f32, stream);
-  } else if constexpr (DK <= kStreamFixMaxDk) {
-    if (half) launch_fix<DK, true>(a, BH, out_f32, stream);
-    else launch_fix<DK, false>(a, BH, out_f32, stream);
-  } else {
-    if (half) launch_rescale<DK, true>(a, BH, out_f32, stream);
-    else launch_rescale<DK, false>(a, BH, out_f32, stream);
-  }
-  return hipGetLastError();
+  if (short_path)
+    return half ? launch_short<DK, true>(a, BH, out_f32, stream)
+                : launch_short<DK, false>(a, BH, out_f32, stream);
+  if constexpr (DK <= kStreamFixMaxDk)
+    return half ? launch_fix<DK, true>(a, BH, out_f32, stream)
+                : launch_fix<DK, false>(a, BH, out_f32, stream);
+  else
+    return half ? launch_rescale<DK, true>(a, BH, out_f32, stream)
+                : launch_rescale<DK, false>(a, BH, out_f32, stream);
 }
 
 }  // namespace
 
+// Entry for one head-dim class (DK = head dim rounded up to 16).
+template <int DK>
+hipError_t launch_16_dk(const Args16 &a, int BH, bool short_path, bool out_f32, bool half,
+                        hipStream_t stream) {
+  return launch_dk<DK>(a, BH, short_path, out_f32, half, stream);
+}
+
+// The build compiles this file once per head-dim class (-DSDATTN_DK=16 ...
+// 256, in parallel) and once with -DSDATTN_DK=0 for the dispatcher below;
+// compiled without SDATTN_DK it holds everything.
+#define SDATTN_FOR_EACH_DK(X) \
+  X(16) X(32) X(48) X(64) X(80) X(96) X(112) X(128) X(144) X(160) X(176) X(192) X(208) \
+  X(224) X(240) X(256)
+#define SDATTN_INST(DK)                                                                  \
+  template hipError_t launch_16_dk<DK>(const Args16 &, int, bool, bool, bool, hipStream_t);
+#define SDATTN_EXTERN(DK)                                                                \
+  extern template hipError_t launch_16_dk<DK>(const Args16 &, int, bool, bool, bool,    \
+                                              hipStream_t);
+#if defined(SDATTN_DK)
+#if SDATTN_DK > 0
+SDATTN_INST(SDATTN_DK)
+#else
+SDATTN_FOR_EACH_DK(SDATTN_EXTERN)
+#endif
+#else
+SDATTN_FOR_EACH_DK(SDATTN_INST)
+#endif
+
+#if !defined(SDATTN_DK) || SDATTN_DK == 0
 int short_path_max_keys(int d) {
   (void)d;
   return short_cap<16>();
@@ -1415,24 +1423,13 @@ hipError_t launch_16(const Args16 &a, int BH, bool short_path, bool out_f32, boo
                      hipStream_t stream) {
   const int dk = (a.d + 15) / 16 * 16;
   switch (dk) {
-    case 16: return launch_dk<16>(a, BH, short_path, out_f32, half, stream);
-    case 32: return launch_dk<32>(a, BH, short_path, out_f32, half, stream);
-    case 48: return launch_dk<48>(a, BH, short_path, out_f32, half, stream);
-    case 64: return launch_dk<64>(a, BH, short_path, out_f32, half, stream);
-    case 80: return launch_dk<80>(a, BH, short_path, out_f32, half, stream);
-    case 96: return launch_dk<96>(a, BH, short_path, out_f32, half, stream);
-    case 112: return launch_dk<112>(a, BH, short_path, out_f32, half, stream);
-    case 128: return launch_dk<128>(a, BH, short_path, out_f32, half, stream);
-    case 144: return launch_dk<144>(a, BH, short_path, out_f32, half, stream);
-    case 160: return launch_dk<160>(a, BH, short_path, out_f32, half, stream);
-    case 176: return launch_dk<176>(a, BH, short_path, out_f32, half, stream);
-    case 192: return launch_dk<192>(a, BH, short_path, out_f32, half, stream);
-    case 208: return launch_dk<208>(a, BH, short_path, out_f32, half, stream);
-    case 224: return launch_dk<224>(a, BH, short_path, out_f32, half, stream);
-    case 240: return launch_dk<240>(a, BH, short_path, out_f32, half, stream);
-    case 256: return launch_dk<256>(a, BH, short_path, out_f32, half, stream);
+#define SDATTN_CASE(DK) \
+  case DK: return launch_16_dk<DK>(a, BH, short_path, out_f32, half, stream);
+    SDATTN_FOR_EACH_DK(SDATTN_CASE)
+#undef SDATTN_CASE
     default: return hipErrorInvalidValue;
   }
 }
+#endif
 
 }  // namespace sdattn
