@@ -157,3 +157,71 @@ def test_group_norm_random(dev, i):
     else:
         y = _run(w, x, dev, out_dtype=torch.float32)
         _check(y.cpu().numpy().astype(np.float64), want, "f32", f"random {i}")
+
+
+@pytest.mark.parametrize("where", ["first", "middle"])
+@pytest.mark.parametrize("N,C,H,W,G,in_place", [
+    (2, 320, 64, 64, 32, False),    # split form, slice in registers
+    (1, 32, 128, 128, 1, False),    # split form, slice streamed again
+    (2, 320, 128, 128, 32, True),   # streaming form (groups > 65536 elements)
+    (2, 64, 32, 32, 32, True),      # register-resident form
+])
+def test_group_norm_outlier(dev, N, C, H, W, G, in_place, where):
+    """One value per group 50 standard deviations above the rest -- as the
+    group's first element (the shift of the first thread's sums) or in its
+    middle: the moments must not cancel, whichever value a thread's sums
+    are taken about."""
+    import torch
+    import unet_attention_amd as sd
+    r = np.random.default_rng(31000 + N * C + H + G)
+    x = (1.5 + 2.0 * r.standard_normal((N, C, H * W))).astype(np.float32)
+    cpg = C // G
+    xg = x.reshape(N, G, cpg * H * W)
+    pos = 0 if where == "first" else (cpg * H * W) // 2 + 3
+    xg[:, :, pos] += np.float32(100.0)
+    gamma = (1.0 + 0.25 * r.standard_normal(C)).astype(np.float32)
+    beta = (0.5 * r.standard_normal(C)).astype(np.float32)
+    want = oracle.group_norm(x, gamma, beta, G, 1e-5, True)
+    tx = torch.from_numpy(x).to(dev)
+    say(f"group norm outlier {where} N={N} C={C} HW={H * W} G={G} in_place={in_place}")
+    y = sd.group_norm(tx, torch.from_numpy(gamma).to(dev), torch.from_numpy(beta).to(dev), G,
+                      eps=1e-5, silu=True, out=tx if in_place else None)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    e = np.abs(got - want)
+    say(f"group norm outlier max err {e.max():.3e}")
+    # The outlier's own output is ~50: the fp32 statistics carry a relative
+    # summation error of a few 1e-6 (sequential per-thread sums of up to a
+    # few hundred values, then a merge tree), which that output scales.  So
+    # the gate is 1e-4 absolute plus 1e-5 relative.  Sums taken about one
+    # shift for the whole group lose ~1e-4 of the variance to cancellation
+    # here and miss this gate by an order of magnitude.
+    assert np.all(np.isfinite(got))
+    worst = float((e - 1e-5 * np.abs(want)).max())
+    assert worst <= GN_F32_MAX, f"outlier {where} {N},{C},{H},{W},{G}: {worst:.3e}"
+
+
+def test_group_norm_side_stream_bf16_affine(dev):
+    """bf16 gamma/beta converted by the binding and an output it allocates,
+    all for a kernel on a stream other than torch's current one: the
+    conversions and the allocation must be ordered before the kernel."""
+    import torch
+    import unet_attention_amd as sd
+    w = GN_WORKLOADS["gn64"]
+    x = make_gn_inputs(w)
+    gb = torch.from_numpy(x.gamma).to(dev).to(torch.bfloat16)
+    bb = torch.from_numpy(x.beta).to(dev).to(torch.bfloat16)
+    g64 = gb.float().cpu().numpy()
+    b64 = bb.float().cpu().numpy()
+    want = oracle.group_norm(x.x, g64, b64, w.G, w.eps, w.silu)
+    tx = _device_x(x, dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    say("group norm on a side stream, bf16 gamma/beta")
+    ys = []
+    for _ in range(3):
+        ys.append(sd.group_norm(tx, gb, bb, w.G, eps=w.eps, silu=w.silu,
+                                out_dtype=torch.float32, stream=s.cuda_stream))
+    s.synchronize()
+    for y in ys:
+        _check(y.cpu().numpy().astype(np.float64), want, "f32", "side stream")

@@ -13,8 +13,12 @@
 //   registers (fp32), so the mean and the centred variance are exact
 //   two-pass reductions on chip (wave shuffles, then one LDS exchange) and
 //   the output is written once: the minimum traffic, one read and one write;
-// * larger groups stream twice: shifted sums (about the group's first
-//   element) for the statistics, then the normalising pass;
+// * larger groups stream twice: moments for the statistics, then the
+//   normalising pass.  Each thread sums its values shifted by its own first
+//   value (so its sums cancel by at most a factor n + 1 for its n values),
+//   and the per-thread (count, mean, M2) are merged pairwise with Chan's
+//   update, which stays exact-in-form however far apart the partial means
+//   are;
 // * out of place, when there are fewer groups than CUs, several workgroups
 //   share a group: each forms the group's statistics (from L2 after the
 //   first read) and normalises its own slice;
@@ -98,6 +102,53 @@ __device__ __forceinline__ float block_sum(float x, float *red) {
   return t;
 }
 
+// Count, mean and sum of squared deviations of a set of values.
+struct Moments {
+  float n, mean, m2;
+};
+
+// Moments of the union of two disjoint sets (Chan, Golub and LeVeque's
+// pairwise update).  Either set may be empty.
+__device__ __forceinline__ Moments merge_moments(Moments a, Moments b) {
+  const float n = a.n + b.n;
+  if (n == 0.f) return a;
+  const float dl = b.mean - a.mean;
+  const float fb = b.n / n;
+  return Moments{n, __builtin_fmaf(dl, fb, a.mean), a.m2 + b.m2 + dl * dl * a.n * fb};
+}
+
+// A thread's moments from its n values' sums about the shift x0:
+// s1 = sum(x - x0), s2 = sum((x - x0)^2).
+__device__ __forceinline__ Moments moments_from_shifted(float n, float x0, float s1, float s2) {
+  if (n == 0.f) return Moments{0.f, 0.f, 0.f};
+  const float d1 = s1 / n;
+  return Moments{n, x0 + d1, fmaxf(s2 - s1 * d1, 0.f)};
+}
+
+// Moments of the whole workgroup's values, identical in every thread:
+// pairwise merges across the wave, then the waves' results in wave order.
+// red holds 3 * kGnWaves floats; the leading barrier keeps an earlier use
+// of red safe.
+__device__ __forceinline__ Moments block_moments(Moments m, float *red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const Moments o{__shfl_xor(m.n, off), __shfl_xor(m.mean, off), __shfl_xor(m.m2, off)};
+    m = merge_moments(m, o);
+  }
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    const int w = threadIdx.x / kWave;
+    red[3 * w] = m.n;
+    red[3 * w + 1] = m.mean;
+    red[3 * w + 2] = m.m2;
+  }
+  __syncthreads();
+  Moments t{red[0], red[1], red[2]};
+#pragma unroll
+  for (int w = 1; w < kGnWaves; ++w) t = merge_moments(t, Moments{red[3 * w], red[3 * w + 1], red[3 * w + 2]});
+  return t;
+}
+
 // y * sigmoid(y); the hardware reciprocal (1 ulp) in place of an IEEE
 // division.  e^-y overflowing to +inf gives y * 0, the correct limit.
 __device__ __forceinline__ float silu(float y) {
@@ -134,9 +185,26 @@ __device__ __forceinline__ void normalise_store(const GnArgs &a, size_t e, const
   store8<ET, OUT_F32>(a.y, e, v);
 }
 
+// Chunks of [ja, nch) this thread visits (ja + tid, ja + tid + kGnThreads, ...).
+__device__ __forceinline__ int own_chunks(int ja, int nch) {
+  const int first = ja + (int)threadIdx.x;
+  return first < nch ? (nch - first + kGnThreads - 1) / kGnThreads : 0;
+}
+
+// The first value of chunk j (the first chunk this thread sums), the shift
+// of its sums: being one of the thread's own values, it lies within the
+// thread's spread.  0 for a thread with no chunk (j >= nch).
+template <int ET>
+__device__ __forceinline__ float thread_shift(const void *x, size_t base, int j, int nch) {
+  if (j >= nch) return 0.f;
+  float v[8];
+  load8<ET>(x, base + (size_t)j * 8, v);
+  return v[0];
+}
+
 // Shifted sums s1 += x - x0, s2 += (x - x0)^2 over this thread's chunks
 // ja + tid, ja + tid + kGnThreads, ... of [ja, nch), U chunk loads in flight
-// at a time.
+// at a time (a chunk past the range adds x0, i.e. nothing).
 template <int ET, int U>
 __device__ __forceinline__ void shifted_sums(const void *x, size_t base, int ja, int nch,
                                              float x0, float &s1, float &s2) {
@@ -244,7 +312,7 @@ __global__ __launch_bounds__(kGnThreads) void group_norm_resident(GnArgs a) {
 // shifted by the group's first element, then a second pass that normalises.
 template <int ET, bool OUT_F32, bool SILU>
 __global__ __launch_bounds__(kGnThreads) void group_norm_stream(GnArgs a) {
-  __shared__ float red[kGnWaves];
+  __shared__ float red[3 * kGnWaves];
   extern __shared__ float gb[];
   const int ng = blockIdx.x;
   const int n = ng / a.G, g = ng - n * a.G;
@@ -254,22 +322,18 @@ __global__ __launch_bounds__(kGnThreads) void group_norm_stream(GnArgs a) {
   const int tid = threadIdx.x;
 
   stage_affine(a, g * cpg, cpg, gb);
-  float first[8];
-  load8<ET>(a.x, base, first);
-  const float x0 = first[0];
+  // this thread's chunks are tid, tid + kGnThreads, ...; its shift is the
+  // first value of its first chunk
+  const float x0 = thread_shift<ET>(a.x, base, tid, nch);
   float s1 = 0.f, s2 = 0.f;
   shifted_sums<ET, 8>(a.x, base, 0, nch, x0, s1, s2);
-  const float m = (float)nch * 8.0f;
-  const float S1 = block_sum(s1, red);
-  const float S2 = block_sum(s2, red);
-  const float d1 = S1 / m;
-  const float mu = x0 + d1;
-  const float var = fmaxf(S2 / m - d1 * d1, 0.f);
-  const float rstd = 1.0f / sqrtf(var + a.eps);
+  const Moments mo = block_moments(
+      moments_from_shifted(8.0f * (float)own_chunks(0, nch), x0, s1, s2), red);
+  const float mu = mo.mean;
+  const float rstd = 1.0f / sqrtf(mo.m2 / mo.n + a.eps);
   // In place, each chunk is read and then written by the same thread after
   // every read of the statistics pass (the block sums are barriers).
   normalise_range<ET, OUT_F32, SILU, 4>(a, base, 0, nch, gb, cpg, mu, rstd);
-  (void)tid;
 }
 
 // Split form (out of place only): K = a.split workgroups per group, placed on
@@ -280,7 +344,7 @@ __global__ __launch_bounds__(kGnThreads) void group_norm_stream(GnArgs a) {
 // slice's writes would race with the other workgroups' statistics reads.
 template <int ET, bool OUT_F32, bool SILU>
 __global__ __launch_bounds__(kGnThreads) void group_norm_split(GnArgs a) {
-  __shared__ float red[kGnWaves];
+  __shared__ float red[3 * kGnWaves];
   extern __shared__ float gb[];
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int K = a.split;
@@ -292,12 +356,14 @@ __global__ __launch_bounds__(kGnThreads) void group_norm_split(GnArgs a) {
   const int tid = threadIdx.x;
 
   stage_affine(a, g * cpg, cpg, gb);
-  float first[8];
-  load8<ET>(a.x, base, first);
-  const float x0 = first[0];
   const int j0 = (int)((long long)k * nch / K), j1 = (int)((long long)(k + 1) * nch / K);
-  const float m = (float)nch * 8.0f;
   if (j1 - j0 <= kSliceChunks * kGnThreads) {
+    // this thread sums its slice chunks, then its chunks of [0, j0) and of
+    // [j1, nch); its shift is the first of these
+    const int jf = (j0 + tid < j1) ? j0 + tid : (tid < j0) ? tid : j1 + tid;
+    const float x0 = thread_shift<ET>(a.x, base, jf, nch);
+    const float nt =
+        8.0f * (float)(own_chunks(j0, j1) + own_chunks(0, j0) + own_chunks(j1, nch));
     // This workgroup's slice stays in registers from the statistics pass to
     // the normalisation (read once; its loads overlap the rest of the group).
     const int cpc = a.S / 8;
@@ -321,12 +387,9 @@ __global__ __launch_bounds__(kGnThreads) void group_norm_split(GnArgs a) {
         }
       }
     }
-    const float S1 = block_sum(s1, red);
-    const float S2 = block_sum(s2, red);
-    const float d1 = S1 / m;
-    const float mu = x0 + d1;
-    const float var = fmaxf(S2 / m - d1 * d1, 0.f);
-    const float rstd = 1.0f / sqrtf(var + a.eps);
+    const Moments mo = block_moments(moments_from_shifted(nt, x0, s1, s2), red);
+    const float mu = mo.mean;
+    const float rstd = 1.0f / sqrtf(mo.m2 / mo.n + a.eps);
 #pragma unroll
     for (int u = 0; u < kSliceChunks; ++u) {
       const int j = j0 + tid + u * kGnThreads;
@@ -336,14 +399,13 @@ __global__ __launch_bounds__(kGnThreads) void group_norm_split(GnArgs a) {
     }
     return;
   }
+  const float x0 = thread_shift<ET>(a.x, base, tid, nch);
   float s1 = 0.f, s2 = 0.f;
   shifted_sums<ET, 8>(a.x, base, 0, nch, x0, s1, s2);
-  const float S1 = block_sum(s1, red);
-  const float S2 = block_sum(s2, red);
-  const float d1 = S1 / m;
-  const float mu = x0 + d1;
-  const float var = fmaxf(S2 / m - d1 * d1, 0.f);
-  const float rstd = 1.0f / sqrtf(var + a.eps);
+  const Moments mo =
+      block_moments(moments_from_shifted(8.0f * (float)own_chunks(0, nch), x0, s1, s2), red);
+  const float mu = mo.mean;
+  const float rstd = 1.0f / sqrtf(mo.m2 / mo.n + a.eps);
   normalise_range<ET, OUT_F32, SILU, 4>(a, base, j0, j1, gb, cpg, mu, rstd);
 }
 
@@ -352,24 +414,20 @@ hipError_t launch_gn_et(const GnArgs &a, hipStream_t stream) {
   const int nch = a.C / a.G * a.S / 8;
   const dim3 grid(a.N * a.G), block(kGnThreads);
   const size_t lds = 2 * sizeof(float) * (a.C / a.G);  // the group's gamma and beta
-  if (a.split > 1) {
-    hipLaunchKernelGGL((group_norm_split<ET, OUT_F32, SILU>), dim3(a.N * a.G * a.split), block,
-                       lds, stream, a);
-    return hipGetLastError();
-  }
+  if (a.split > 1)
+    return launch_kernel(&group_norm_split<ET, OUT_F32, SILU>, dim3(a.N * a.G * a.split), block,
+                         lds, stream, a);
   const int kpt = (nch + kGnThreads - 1) / kGnThreads;
   if (kpt <= 2)
-    hipLaunchKernelGGL((group_norm_resident<ET, OUT_F32, SILU, 2>), grid, block, lds, stream, a);
-  else if (kpt <= 4)
-    hipLaunchKernelGGL((group_norm_resident<ET, OUT_F32, SILU, 4>), grid, block, lds, stream, a);
-  else if (kpt <= 8)
-    hipLaunchKernelGGL((group_norm_resident<ET, OUT_F32, SILU, 8>), grid, block, lds, stream, a);
-  else if (kpt <= kMaxChunksPerThread)
-    hipLaunchKernelGGL((group_norm_resident<ET, OUT_F32, SILU, kMaxChunksPerThread>), grid,
-                       block, lds, stream, a);
-  else
-    hipLaunchKernelGGL((group_norm_stream<ET, OUT_F32, SILU>), grid, block, lds, stream, a);
-  return hipGetLastError();
+    return launch_kernel(&group_norm_resident<ET, OUT_F32, SILU, 2>, grid, block, lds, stream, a);
+  if (kpt <= 4)
+    return launch_kernel(&group_norm_resident<ET, OUT_F32, SILU, 4>, grid, block, lds, stream, a);
+  if (kpt <= 8)
+    return launch_kernel(&group_norm_resident<ET, OUT_F32, SILU, 8>, grid, block, lds, stream, a);
+  if (kpt <= kMaxChunksPerThread)
+    return launch_kernel(&group_norm_resident<ET, OUT_F32, SILU, kMaxChunksPerThread>, grid,
+                         block, lds, stream, a);
+  return launch_kernel(&group_norm_stream<ET, OUT_F32, SILU>, grid, block, lds, stream, a);
 }
 
 template <int ET, bool OUT_F32>
