@@ -115,6 +115,20 @@ def sdattn_version():
 # ---------------------------------------------------------------------------
 # torch tensors in, torch tensors out
 
+
+def _on_stream(stream, device):
+    """(hipStream_t handle, context) for a call: the caller's stream handle
+    (an int) or, if None, torch's current stream.  Under the context, torch
+    allocates and converts on that same stream, so every temporary and the
+    output are ordered before the kernel that reads or writes them (and the
+    caching allocator does not hand their memory to other streams early)."""
+    import contextlib
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream, contextlib.nullcontext()
+    ext = torch.cuda.ExternalStream(stream, device=device)
+    return stream, torch.cuda.stream(ext)
+
 _ENTRIES = {"auto": "sdattn_fwd", "cross": "sdattn_cross_fwd",
             "stream": "sdattn_stream_fwd"}
 
@@ -150,17 +164,18 @@ def _call(entry, q, k, v, out=None, scale=None, out_dtype=None, stream=None):
     Lk = k.shape[2]
     if tuple(k.shape) != (B, H, Lk, d) or tuple(v.shape) != (B, H, Lk, d):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    if out is None:
-        out = torch.empty((B, H, Lq, d), dtype=odt, device=q.device)
-    elif out.dtype != odt or tuple(out.shape) != (B, H, Lq, d) or not out.is_contiguous():
+    if out is not None and (out.dtype != odt or tuple(out.shape) != (B, H, Lq, d)
+                            or not out.is_contiguous()):
         raise ValueError("out must be a contiguous [B,H,Lq,d] tensor of the output dtype")
     if scale is None:
         scale = float(1.0 / math.sqrt(d))
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
     fn = getattr(load(), _ENTRIES[entry])
-    rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            B, H, Lq, Lk, d, scale, dtype_code, stream)
+    handle, ctx = _on_stream(stream, q.device)
+    with ctx:
+        if out is None:
+            out = torch.empty((B, H, Lq, d), dtype=odt, device=q.device)
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                B, H, Lq, Lk, d, scale, dtype_code, handle)
     if rc != SDATTN_OK:
         raise SdattnError(rc, _ENTRIES[entry])
     return out
@@ -207,18 +222,18 @@ def fwd_tokens(q, k, v, heads, out=None, scale=None, out_dtype=None, stream=None
     d = C // heads
     if tuple(k.shape) != (B, Lk, C) or tuple(v.shape) != (B, Lk, C):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    if out is None:
-        out = torch.empty((B, Lq, C), dtype=odt, device=q.device)
-    elif out.dtype != odt or tuple(out.shape) != (B, Lq, C) or out.stride(2) != 1 or \
-            out.stride(0) != Lq * out.stride(1):
+    if out is not None and (out.dtype != odt or tuple(out.shape) != (B, Lq, C)
+                            or out.stride(2) != 1 or out.stride(0) != Lq * out.stride(1)):
         raise ValueError("out must be a [B, Lq, C] tensor of the output dtype")
     if scale is None:
         scale = float(1.0 / math.sqrt(d))
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = load().sdattn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                   B, heads, Lq, Lk, d, q.stride(1), k.stride(1),
-                                   out.stride(1), scale, dtype_code, stream)
+    handle, ctx = _on_stream(stream, q.device)
+    with ctx:
+        if out is None:
+            out = torch.empty((B, Lq, C), dtype=odt, device=q.device)
+        rc = load().sdattn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       B, heads, Lq, Lk, d, q.stride(1), k.stride(1),
+                                       out.stride(1), scale, dtype_code, handle)
     if rc != SDATTN_OK:
         raise SdattnError(rc, "sdattn_fwd_strided")
     return out
@@ -235,19 +250,21 @@ def group_norm(x, gamma, beta, groups, eps=1e-5, silu=False, out=None, out_dtype
         raise ValueError("x must be a contiguous [N, C, ...] device tensor")
     N, C = x.shape[0], x.shape[1]
     HW = x.numel() // max(1, N * C)
-    g = gamma.to(device=x.device, dtype=torch.float32).contiguous()
-    b = beta.to(device=x.device, dtype=torch.float32).contiguous()
-    if g.numel() != C or b.numel() != C:
+    if gamma.numel() != C or beta.numel() != C:
         raise ValueError("gamma and beta must have C entries")
-    if out is None:
-        out = torch.empty(x.shape, dtype=odt, device=x.device)
-    elif out.dtype != odt or out.shape != x.shape or not out.is_contiguous():
+    if out is not None and (out.dtype != odt or out.shape != x.shape or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor of x's shape and the output dtype")
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    rc = load().sdattn_group_norm(x.data_ptr(), g.data_ptr(), b.data_ptr(), out.data_ptr(),
-                                  N, C, HW, groups, float(eps), int(bool(silu)), dtype_code,
-                                  stream)
+    handle, ctx = _on_stream(stream, x.device)
+    with ctx:
+        # fp32 copies of gamma and beta (when they are not fp32 already) are
+        # made on the launch stream, so the kernel runs after them
+        g = gamma.to(device=x.device, dtype=torch.float32).contiguous()
+        b = beta.to(device=x.device, dtype=torch.float32).contiguous()
+        if out is None:
+            out = torch.empty(x.shape, dtype=odt, device=x.device)
+        rc = load().sdattn_group_norm(x.data_ptr(), g.data_ptr(), b.data_ptr(), out.data_ptr(),
+                                      N, C, HW, groups, float(eps), int(bool(silu)), dtype_code,
+                                      handle)
     if rc != SDATTN_OK:
         raise SdattnError(rc, "sdattn_group_norm")
     return out
