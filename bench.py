@@ -19,8 +19,13 @@ Input sets are rotated across more than 512 MB of buffers so that the
 HBM-bound cross-attention kernel is not served from the 256 MB Infinity
 Cache (a warm-cache figure for the same kernels is reported separately).
 
+The line also carries the chip's attainable rates measured in the same run
+(dense bf16 MFMA with and without softmax-like vector work beside it, device
+copies of the step's size and of 1 GiB, LDS reads), the GPU clock and power
+sampled while the step runs, and per-launch median and minimum times.
+
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
-       [--no-cpu-baseline] [--copy-calibration]
+       [--no-cpu-baseline] [--no-peaks] [--copy-calibration] [--suite]
 """
 from __future__ import annotations
 
@@ -90,6 +95,10 @@ def parse():
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the attainable-peak microbenchmarks")
+    ap.add_argument("--suite", action="store_true",
+                    help="run every row of SUITE a few times (for profiler runs) and exit")
     return ap.parse_args()
 
 
@@ -106,6 +115,212 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
+# Rows run by --suite (one process, so a profiler pass covers every row):
+# each row is a step name; kernel launches happen in this order.
+SUITE = ["sd15_64x64_block", "sd15_64x64_block_f16", "workload_4a", "workload_4b",
+         "workload_4c", "workload_4d", "workload_5", "workload_6a", "workload_6b"]
+SUITE_GN = ["gn64", "gn128"]
+
+
+class Step:
+    """Device buffers and C-ABI argument tuples for one step: input sets are
+    rotated over more than ROTATE_BYTES so HBM-bound kernels read HBM."""
+
+    def __init__(self, torch, sd, name, stream, rotate=True):
+        self.name = name
+        self.calls = STEPS[name]
+        self.ws = [WORKLOADS[n] for n, _ in self.calls]
+        self.inputs = [make_inputs(w) for w in self.ws]
+        elt = self.ws[0].dtype  # one element type per step
+        assert all(w.dtype == elt for w in self.ws) and elt in ("bf16", "f16")
+        self.elt = elt
+        tdt = torch.bfloat16 if elt == "bf16" else torch.float16
+        code = sd.SDATTN_DTYPE_BF16 if elt == "bf16" else sd.SDATTN_DTYPE_F16
+        dev = torch.device("cuda:0")
+
+        def dev16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
+
+        base = [tuple(dev16(b) for b in (x.q_bits, x.k_bits, x.v_bits)) for x in self.inputs]
+        self.set_bytes = sum(2 * (q.numel() + k.numel() + v.numel() + q.numel())
+                             for q, k, v in base)
+        self.nsets = max(2, -(-ROTATE_BYTES // self.set_bytes)) if rotate else 1
+        self.sets = []
+        for s in range(self.nsets):
+            self.sets.append([((q, k, v) if s == 0 else (q.clone(), k.clone(), v.clone()))
+                              + (torch.empty_like(q),) for q, k, v in base])
+        torch.cuda.synchronize()
+        lib = sd.load()
+        fns = {"fwd": lib.sdattn_fwd, "cross": lib.sdattn_cross_fwd}
+        sh = stream.cuda_stream
+        self.argv = [[(fns[entry], (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    w.B, w.H, w.Lq, w.Lk, w.d, w.scale, code, sh))
+                      for (n, entry), w, (q, k, v, o) in zip(self.calls, self.ws, row)]
+                     for row in self.sets]
+        self._sd = sd
+
+    def launch_set(self, i):
+        for fn, a in self.argv[i % self.nsets]:
+            rc = fn(*a)
+            if rc != self._sd.SDATTN_OK:
+                raise self._sd.SdattnError(rc, "bench launch")
+
+
+def sample_clock(run_for, seconds=0.4):
+    """GPU clock (MHz, first XCD's GFX clock as amd-smi reports it) and socket
+    power (W) sampled every ~5 ms while run_for(seconds) keeps the GPU busy."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # no amd-smi: report why
+        run_for(seconds)
+        return {"error": f"amdsmi unavailable: {e}"}
+    clk, pw, stop = [], [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                clk.append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+                pw.append(amdsmi.amdsmi_get_power_info(h)["current_socket_power"])
+            except Exception:
+                pass
+            time.sleep(0.005)
+
+    t = threading.Thread(target=poll)
+    t.start()
+    try:
+        run_for(seconds)
+    finally:
+        stop.set()
+        t.join()
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+    # drop the first and last tenth (ramp up / drain)
+    k = len(clk) // 10
+    c = [x for x in clk[k:len(clk) - k] if isinstance(x, (int, float))] or clk
+    p_ = [x for x in pw[k:len(pw) - k] if isinstance(x, (int, float))] or pw
+    num = lambda v: [x for x in v if isinstance(x, (int, float))]
+    return {"gfx_mhz_median": float(np.median(num(c))) if num(c) else None,
+            "gfx_mhz_min": float(np.min(num(c))) if num(c) else None,
+            "socket_w_median": float(np.median(num(p_))) if num(p_) else None,
+            "samples": len(clk), "source": "amdsmi (GFX clock of the first XCD)"}
+
+
+def attainable_peaks(torch, stream, copy_bytes):
+    """The chip's attainable rates in this run (libsdattn_peak.so): dense bf16
+    MFMA alone and with n exp2 + n add (the softmax's per-score vector work)
+    or n FMA per matrix instruction; device copies of copy_bytes of traffic
+    (rotated over > 512 MB, so from HBM) and of 1 GiB; LDS 16-byte reads."""
+    import ctypes
+    from unet_attention_amd import build as hb
+    if not os.path.exists(hb.PEAK_LIB):
+        return {"error": "libsdattn_peak.so not built"}
+    lib = ctypes.CDLL(hb.PEAK_LIB)
+    lib.peak_mfma.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong,
+                              ctypes.c_int, ctypes.c_void_p]
+    lib.peak_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sh = stream.cuda_stream
+
+    def timed(launch, reps):
+        launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    out = {}
+    nwg, iters = 512, 8000   # 2 waves per SIMD
+    sink = torch.empty(nwg * 256, dtype=torch.float32, device="cuda")
+    flops = nwg * 4 * iters * 4 * 2 * 32 * 32 * 16
+    mf = {}
+    for ne, nf in ((0, 0), (2, 0), (4, 0), (8, 0), (0, 4), (0, 8), (2, 4), (4, 4)):
+        def go(ne=ne, nf=nf):
+            rc = lib.peak_mfma(nwg, iters, ne, nf, sink.data_ptr(), sh)
+            if rc:
+                raise RuntimeError(f"peak_mfma failed ({rc})")
+        mf[f"exp{ne}_fma{nf}"] = round(flops / timed(go, 3) / 1e12, 1)
+    out["mfma_bf16_tflops"] = mf.pop("exp0_fma0")
+    out["mfma_bf16_tflops_with_vector_work_per_mfma"] = mf
+    # copies: copy_bytes of traffic (half read, half written), rotated
+    half = (copy_bytes // 2) // 16 * 16
+    nbuf = max(2, -(-ROTATE_BYTES // (2 * half)))
+    bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
+             torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(nbuf)]
+    for a_, b_ in bufs:
+        a_.fill_(1)
+    ci = [0]
+
+    def cp():
+        a_, b_ = bufs[ci[0] % nbuf]
+        ci[0] += 1
+        rc = lib.peak_copy(a_.data_ptr(), b_.data_ptr(), half, 2048, sh)
+        if rc:
+            raise RuntimeError(f"peak_copy failed ({rc})")
+    t_small = timed(cp, 4 * nbuf)
+    out["copy"] = {f"{2 * half / 1e6:.2f}MB_us": round(t_small * 1e6, 2),
+                   f"{2 * half / 1e6:.2f}MB_gbs": round(2 * half / t_small / 1e9, 1)}
+    del bufs
+    big = 1 << 30
+    a_ = torch.empty(big, dtype=torch.uint8, device="cuda")
+    b_ = torch.empty(big, dtype=torch.uint8, device="cuda")
+    a_.fill_(1)
+    t_big = timed(lambda: lib.peak_copy(a_.data_ptr(), b_.data_ptr(), big, 4096, sh), 5)
+    out["copy"]["1GiB_gbs"] = round(2 * big / t_big / 1e9, 1)
+    del a_, b_
+    lnwg, liters = 1024, 4000
+    lsink = torch.empty(lnwg * 256, dtype=torch.float32, device="cuda")
+    t_lds = timed(lambda: lib.peak_lds(lnwg, liters, lsink.data_ptr(), sh), 3)
+    out["lds_read_gbs"] = round(lnwg * 256 * liters * 8 * 16 / t_lds / 1e9, 1)
+    out["method"] = ("HIP events around back-to-back launches; MFMA: 512 workgroups of 4 waves, "
+                     "v_mfma_f32_32x32x16_bf16 on 4 accumulators per wave; copies with 16-byte "
+                     "lanes")
+    return out
+
+
+def load_kernel_profile(step_name: str):
+    """Kernel-only durations (rocprofv3 averages) from the committed trace
+    summary of this step, if the kernel sources have not changed since."""
+    path = os.path.join(ROOT, "profiles", f"trace_{step_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("kernels")
+
+
+def suite(args, torch, sd):
+    """Every SUITE row (and the GroupNorm rows) a few times each, in a fixed
+    order, for profiler passes: warmup launches, then args.steps launches."""
+    stream = torch.cuda.current_stream()
+    for name in SUITE:
+        st = Step(torch, sd, name, stream, rotate=name != "workload_5")
+        n = args.steps if name != "workload_5" else max(1, args.steps // 4)
+        for i in range(args.warmup + n):
+            st.launch_set(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"suite_row": name, "launches_per_call": args.warmup + n,
+                          "calls": [f"{e} {w.name}" for (_, e), w in zip(st.calls, st.ws)]}),
+              flush=True)
+        del st
+        torch.cuda.empty_cache()
+    for name in SUITE_GN:
+        args.workload = f"gn_{name}"
+        bench_group_norm(args, name, quiet=True)
+        print(json.dumps({"suite_row": f"gn_{name}", "launches_per_call": args.warmup + args.steps}),
+              flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -119,111 +334,96 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    sd.load()
+    if args.suite:
+        suite(args, torch, sd)
+        return
     if args.workload.startswith("gn_"):
         bench_group_norm(args, args.workload[3:])
         return
     if args.copy_calibration:
         copy_calibration()
         return
-    sd.load()
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
+    stream = torch.cuda.current_stream(torch.device("cuda:0"))
+    st = Step(torch, sd, args.workload, stream)
+    calls, ws, nsets = st.calls, st.ws, st.nsets
 
-    calls = STEPS[args.workload]
-    ws = [WORKLOADS[n] for n, _ in calls]
-    inputs = [make_inputs(w) for w in ws]
-
-    elt = ws[0].dtype  # "bf16" or "f16"; one element type per step
-    assert all(w.dtype == elt for w in ws) and elt in ("bf16", "f16")
-    tdt = torch.bfloat16 if elt == "bf16" else torch.float16
-    dtype_code = sd.SDATTN_DTYPE_BF16 if elt == "bf16" else sd.SDATTN_DTYPE_F16
-
-    def dev16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
-
-    base = [tuple(dev16(b) for b in (x.q_bits, x.k_bits, x.v_bits)) for x in inputs]
-    set_bytes = sum(2 * (q.numel() + k.numel() + v.numel() + q.numel()) for q, k, v in base)
-    nsets = max(2, -(-ROTATE_BYTES // set_bytes))
-    sets = []
-    for s in range(nsets):
-        one = []
-        for (q, k, v), w in zip(base, ws):
-            qq, kk, vv = (q, k, v) if s == 0 else (q.clone(), k.clone(), v.clone())
-            out = torch.empty_like(qq)
-            one.append((qq, kk, vv, out))
-        sets.append(one)
-    torch.cuda.synchronize()
-
-    fns = {"fwd": sd.load().sdattn_fwd, "cross": sd.load().sdattn_cross_fwd}
-    argv = []
-    for s in range(nsets):
-        row = []
-        for (n, entry), w, (q, k, v, o) in zip(calls, ws, sets[s]):
-            row.append((fns[entry], (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                     w.B, w.H, w.Lq, w.Lk, w.d, w.scale,
-                                     dtype_code, sh)))
-        argv.append(row)
-
-    def launch(fn, a):
-        rc = fn(*a)
-        if rc != sd.SDATTN_OK:
-            raise sd.SdattnError(rc, "bench launch")
-
-    # warmup
     for i in range(args.warmup):
-        for fn, a in argv[i % nsets]:
-            launch(fn, a)
+        st.launch_set(i)
     torch.cuda.synchronize()
 
     # timed region: one event on the launch stream before every call and one
     # after the last, so each call is timed between consecutive events (an
-    # event pair around every call would add its own GPU time to the step)
+    # event pair around every call would add its own GPU time to the step);
+    # a call's interval therefore also holds the gap to the next launch
     K = args.steps
     nc = len(calls)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(K * nc + 1)]
     torch.cuda.synchronize()
     for i in range(K):
-        for j, (fn, a) in enumerate(argv[i % nsets]):
+        for j, (fn, a) in enumerate(st.argv[i % nsets]):
             ev[i * nc + j].record(stream)
-            launch(fn, a)
+            rc = fn(*a)
+            if rc != sd.SDATTN_OK:
+                raise sd.SdattnError(rc, "bench launch")
     ev[K * nc].record(stream)
     torch.cuda.synchronize()
     ms_step = ev[0].elapsed_time(ev[K * nc]) / K
-    per_call_ms = [float(np.mean([ev[i * nc + j].elapsed_time(ev[i * nc + j + 1])
-                                  for i in range(K)])) for j in range(nc)]
+    per_call = [np.array([ev[i * nc + j].elapsed_time(ev[i * nc + j + 1]) for i in range(K)])
+                for j in range(nc)]
+    per_call_ms = [float(x.mean()) for x in per_call]
 
     # warm-cache figure: same kernels, one buffer set
     warm_ms = []
-    for j, (fn, a) in enumerate(argv[0]):
+    for j, (fn, a) in enumerate(st.argv[0]):
         for _ in range(5):
-            launch(fn, a)
+            fn(*a)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         n = 50
         e0.record(stream)
         for _ in range(n):
-            launch(fn, a)
+            fn(*a)
         e1.record(stream)
         torch.cuda.synchronize()
         warm_ms.append(e0.elapsed_time(e1) / n)
 
+    # clock and power while the step runs back to back
+    def run_for(sec):
+        n = max(1, int(sec / (ms_step * 1e-3)))
+        for i in range(n):
+            st.launch_set(i)
+        torch.cuda.synchronize()
+    clock = sample_clock(run_for)
+
     step_flops = sum(w.flops for w in ws)
     value = step_flops / (ms_step * 1e-3) / 1e12
+    prof = load_kernel_profile(args.workload) or {}
 
     kernels = []
-    for (n, entry), w, t_ms, tw in zip(calls, ws, per_call_ms, warm_ms):
-        t = t_ms * 1e-3
+    for (n, entry), w, t_all, tw in zip(calls, ws, per_call, warm_ms):
+        t = float(t_all.mean()) * 1e-3
+        kp = prof.get(n)
         kernels.append({
             "workload": n, "entry": f"sdattn_{entry}" if entry != "fwd" else "sdattn_fwd",
             "shape": f"B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} d{w.d}",
-            "us_per_launch": round(t_ms * 1e3, 3),
+            "us_per_launch": round(t * 1e6, 3),
+            "us_per_launch_median": round(float(np.median(t_all)) * 1e3, 3),
+            "us_per_launch_min": round(float(t_all.min()) * 1e3, 3),
             "tflops": round(w.flops / t / 1e12, 2),
             "gbs_alg": round(w.bytes_alg(2) / t / 1e9, 1),
             "mfma_frac": round(w.flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
             "hbm_frac": round(w.bytes_alg(2) / t / 1e9 / PEAK_HBM_GBS, 4),
             "warm_cache_us": round(tw * 1e3, 3),
+            "timing_note": "event interval to the next launch (includes the launch gap)",
+            "kernel_only_us_rocprof": None if kp is None else kp["avg_us"],
+            "hbm_frac_kernel_only": None if kp is None else
+            round(w.bytes_alg(2) / (kp["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         })
+
+    peaks = None
+    if not args.no_peaks:
+        peaks = attainable_peaks(torch, stream, ws[-1].bytes_alg(2))
 
     # dominant kernel = the call with the largest share of step time
     jd = int(np.argmax(per_call_ms))
@@ -236,6 +436,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic}
+        if peaks and "mfma_bf16_tflops" in peaks:
+            roof["frac_of_attainable"] = round(ach / peaks["mfma_bf16_tflops"], 4)
     else:
         ach = wd.bytes_alg(2) / td / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
@@ -244,60 +446,100 @@ def main():
     roof["flops_per_launch"] = wd.flops
     roof["alg_bytes_per_launch"] = wd.bytes_alg(2)
     roof["us_per_launch"] = kernels[jd]["us_per_launch"]
+    roof["us_per_launch_median"] = kernels[jd]["us_per_launch_median"]
+    roof["us_per_launch_min"] = kernels[jd]["us_per_launch_min"]
 
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
-        cpu, parity = cpu_baseline(args, calls, ws, inputs, sets[0], step_flops)
+        cpu, parity = cpu_baseline(args, calls, ws, st.inputs, st.sets[0], step_flops)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": elt, "data": "synthetic",
+        "dtype": st.elt, "data": "synthetic",
         "config": {"workload": args.workload,
                    "calls": [f"{k['entry']} {k['shape']}" for k in kernels],
-                   "io": f"{elt} in/out, fp32 accumulation",
+                   "io": f"{st.elt} in/out, fp32 accumulation",
                    "buffer_sets_rotated": nsets,
-                   "rotated_bytes": nsets * set_bytes},
+                   "rotated_bytes": nsets * st.set_bytes},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "attainable": peaks,
+        "gpu_clock": clock,
         "parity_vs_oracle": parity,
         "kernel_source_sha": kernel_source_sha(),
     }
     print(json.dumps(line), flush=True)
 
 
+def oracle_threads(args):
+    """Threads for the oracle: --cpu-threads, else OMP_NUM_THREADS (the host's
+    CPU share where it is set), else every core in this process's affinity."""
+    if args.cpu_threads:
+        return args.cpu_threads
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_model():
+    with open("/proc/cpuinfo") as f:
+        return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "?")
+
+
 def cpu_baseline(args, calls, ws, inputs, set0, step_flops):
     """Time the fp64 CPU oracle on the same step (test infrastructure only),
-    and compare the benchmarked GPU output with it."""
+    and compare the benchmarked GPU output with it.  Steps of more than
+    2 TFLOP are timed on a stated row sample (rows are independent and cost
+    the same, so the rate extrapolates); small calls (under 10 GFLOP) are
+    also timed on one thread."""
     import oracle
-    import torch
-    threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+    from workloads import sample_rows
+    threads = oracle_threads(args)
     orc = oracle.get()
-    total = 0.0
-    worst = {}
+    total, flops_done = 0.0, 0
+    worst, single, samples = {}, {}, []
     for (n, _), w, x, (_, _, _, out) in zip(calls, ws, inputs, set0):
         q, k, v = (np.ascontiguousarray(a, dtype=np.float64) for a in (x.q, x.k, x.v))
-        t0 = time.perf_counter()
-        want = orc.attn(q, k, v, w.scale, nthreads=threads)
-        total += time.perf_counter() - t0
         got = out.float().cpu().numpy().astype(np.float64)
-        e = np.abs(got - want)
+        if w.flops > 2e12:
+            rows = sample_rows(w, 2048)
+            t0 = time.perf_counter()
+            want = orc.attn_rows(q, k, v, w.scale, rows, nthreads=threads)
+            total += time.perf_counter() - t0
+            flops_done += 4 * rows.size * w.Lk * w.d
+            e = np.abs(got.reshape(-1, w.d)[rows] - want)
+            samples.append(f"workload {n}: {rows.size} sampled rows of {w.B * w.H * w.Lq}")
+        else:
+            t0 = time.perf_counter()
+            want = orc.attn(q, k, v, w.scale, nthreads=threads)
+            total += time.perf_counter() - t0
+            flops_done += w.flops
+            e = np.abs(got - want)
+            samples.append(f"workload {n}: every row")
+            if w.flops < 10e9:
+                t0 = time.perf_counter()
+                orc.attn(q, k, v, w.scale, nthreads=1)
+                t1 = time.perf_counter() - t0
+                single[n] = {"value": round(w.flops / t1 / 1e12, 6), "unit": "TFLOP/s",
+                             "seconds": round(t1, 3)}
         worst[n] = {"max_abs": float(e.max()), "mean_abs": float(e.mean())}
-    with open("/proc/cpuinfo") as f:
-        model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "?")
-    cpu = {"value": round(step_flops / total / 1e12, 6), "unit": "TFLOP/s",
+    cpu = {"value": round(flops_done / total / 1e12, 6), "unit": "TFLOP/s",
            "cores": threads, "kind": "oracle",
-           "sample": f"one full step ({' + '.join(w.name for w in ws)}), fp64, "
-                     f"{total:.2f} s on {threads} threads of {model}"}
+           "sample": f"{'; '.join(samples)}; fp64, {total:.2f} s on {threads} threads of "
+                     f"{cpu_model()} ({len(os.sched_getaffinity(0))} cores in affinity)",
+           "single_thread": single or None}
     return cpu, worst
 
 
-def bench_group_norm(args, name):
+def bench_group_norm(args, name, quiet=False):
     """GroupNorm (+ SiLU) of one UNet level: an HBM-bound kernel, measured in
-    GB/s of algorithmic traffic (x read once, y written once, gamma/beta)."""
+    GB/s of algorithmic traffic (x read once, y written once, gamma/beta).
+    quiet: launch only (warmup + steps), no timing or output (profiler suite)."""
     import torch
     import unet_attention_amd as sd
     w = GN_WORKLOADS[name]
@@ -329,6 +571,11 @@ def bench_group_norm(args, name):
     for i in range(args.warmup):
         launch(*sets[i % nsets])
     torch.cuda.synchronize()
+    if quiet:
+        for i in range(args.steps):
+            launch(*sets[i % nsets])
+        torch.cuda.synchronize()
+        return
     K = args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K)]
@@ -353,16 +600,14 @@ def bench_group_norm(args, name):
     cpu, parity = None, None
     if not args.no_cpu_baseline:
         import oracle
-        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        threads = oracle_threads(args)
         t = time.perf_counter()
         want = oracle.group_norm(x.x, x.gamma, x.beta, w.G, w.eps, w.silu, nthreads=threads)
         el = time.perf_counter() - t
         got = sets[0][1].float().cpu().numpy().astype(np.float64)
         e = np.abs(got - want)
         parity = {name: {"max_abs": float(e.max()), "mean_abs": float(e.mean())}}
-        with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
-                         "?")
+        model = cpu_model()
         cpu = {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
                "kind": "oracle", "sample": f"the whole workload {name}, fp64, {el:.3f} s on "
                                            f"{threads} threads of {model}"}
