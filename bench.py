@@ -166,24 +166,41 @@ class Step:
                 raise self._sd.SdattnError(rc, "bench launch")
 
 
-def sample_clock(run_for, seconds=0.4):
-    """GPU clock (MHz, first XCD's GFX clock as amd-smi reports it) and socket
-    power (W) sampled every ~5 ms while run_for(seconds) keeps the GPU busy."""
+def sample_clock(run_for, seconds=1.0):
+    """GPU clock (MHz) and socket power (W) sampled every ~5 ms while
+    run_for(seconds) keeps the GPU busy: amd-smi's GFX clock of the first
+    XCD, and the current GFX clock of every XCD from its metrics table."""
     import threading
     try:
         import amdsmi
+        import torch
         amdsmi.amdsmi_init()
-        h = amdsmi.amdsmi_get_processor_handles()[0]
-    except Exception as e:  # no amd-smi: report why
+        # amd-smi may list GPUs this process does not use: take the one whose
+        # PCI address is torch's device 0
+        pr = torch.cuda.get_device_properties(0)
+        want = (pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+        h, bdf = None, None
+        for cand in amdsmi.amdsmi_get_processor_handles():
+            b = amdsmi.amdsmi_get_gpu_device_bdf(cand)
+            dom, bus, rest = b.split(":")
+            if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                h, bdf = cand, b
+                break
+        if h is None:
+            raise RuntimeError(f"no amd-smi device at PCI {want}")
+    except Exception as e:  # no amd-smi or no match: report why
         run_for(seconds)
         return {"error": f"amdsmi unavailable: {e}"}
-    clk, pw, stop = [], [], threading.Event()
+    clk, pw, xcd, stop = [], [], [], threading.Event()
 
     def poll():
         while not stop.is_set():
             try:
                 clk.append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
                 pw.append(amdsmi.amdsmi_get_power_info(h)["current_socket_power"])
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h).get("current_gfxclks")
+                if isinstance(m, (list, tuple)):
+                    xcd.extend(x for x in m if isinstance(x, (int, float)) and 0 < x < 10000)
             except Exception:
                 pass
             time.sleep(0.005)
@@ -206,8 +223,10 @@ def sample_clock(run_for, seconds=0.4):
     num = lambda v: [x for x in v if isinstance(x, (int, float))]
     return {"gfx_mhz_median": float(np.median(num(c))) if num(c) else None,
             "gfx_mhz_min": float(np.min(num(c))) if num(c) else None,
+            "xcd_gfx_mhz_median": float(np.median(xcd)) if xcd else None,
             "socket_w_median": float(np.median(num(p_))) if num(p_) else None,
-            "samples": len(clk), "source": "amdsmi (GFX clock of the first XCD)"}
+            "samples": len(clk), "device_bdf": bdf,
+            "source": "amdsmi: GFX clock of the first XCD; metrics table, every XCD"}
 
 
 def attainable_peaks(torch, stream, copy_bytes):
@@ -262,7 +281,7 @@ def attainable_peaks(torch, stream, copy_bytes):
     def cp():
         a_, b_ = bufs[ci[0] % nbuf]
         ci[0] += 1
-        rc = lib.peak_copy(a_.data_ptr(), b_.data_ptr(), half, 2048, sh)
+        rc = lib.peak_copy(a_.data_ptr(), b_.data_ptr(), half, 1024, sh)
         if rc:
             raise RuntimeError(f"peak_copy failed ({rc})")
     t_small = timed(cp, 4 * nbuf)
@@ -273,7 +292,7 @@ def attainable_peaks(torch, stream, copy_bytes):
     a_ = torch.empty(big, dtype=torch.uint8, device="cuda")
     b_ = torch.empty(big, dtype=torch.uint8, device="cuda")
     a_.fill_(1)
-    t_big = timed(lambda: lib.peak_copy(a_.data_ptr(), b_.data_ptr(), big, 4096, sh), 5)
+    t_big = timed(lambda: lib.peak_copy(a_.data_ptr(), b_.data_ptr(), big, 8192, sh), 5)
     out["copy"]["1GiB_gbs"] = round(2 * big / t_big / 1e9, 1)
     del a_, b_
     lnwg, liters = 1024, 4000
@@ -310,15 +329,17 @@ def suite(args, torch, sd):
             st.launch_set(i)
         torch.cuda.synchronize()
         print(json.dumps({"suite_row": name, "launches_per_call": args.warmup + n,
-                          "calls": [f"{e} {w.name}" for (_, e), w in zip(st.calls, st.ws)]}),
-              flush=True)
+                          "warmup": args.warmup,
+                          "calls": [f"{e} {w.name}" for (_, e), w in zip(st.calls, st.ws)],
+                          "kernel_source_sha": kernel_source_sha()}), flush=True)
         del st
         torch.cuda.empty_cache()
     for name in SUITE_GN:
         args.workload = f"gn_{name}"
         bench_group_norm(args, name, quiet=True)
-        print(json.dumps({"suite_row": f"gn_{name}", "launches_per_call": args.warmup + args.steps}),
-              flush=True)
+        print(json.dumps({"suite_row": f"gn_{name}", "launches_per_call": args.warmup + args.steps,
+                          "warmup": args.warmup, "calls": [f"group_norm {name}"],
+                          "kernel_source_sha": kernel_source_sha()}), flush=True)
 
 
 def main():
