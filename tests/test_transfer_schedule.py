@@ -1,21 +1,26 @@
 """CPU model of the fixed-reference streaming kernel's transfer schedule
 (attn_mfma.hip, attn_stream_fix): which K/V tile transfers each wave issues
-in which iteration, the vmcnt value it waits for at each barrier, and which
-LDS buffer every transfer lands in.
+at which barrier, the vmcnt value it waits for there, and which LDS buffer
+every transfer lands in.
 
-The kernel issues K tile u into buffer u % NB in iteration u - NB and V tile
-u into buffer u % NB in iteration u - NB + 2 (the prologue plays iterations
--NB .. -1); iteration t reads K tile t+1 (scores) and V tile t-1 (P.V).
+Schedule (NB LDS buffers per operand): K tile u goes to buffer u % NB and V
+tile u to buffer u % NB.  Iteration j owns the transfers of K tile j+NB-1
+and V tile j+NB-3 (the prologue plays iterations 1-NB .. -1); iteration t
+reads K tile t+1 (scores) and V tile t-1 (P.V) in its block.  A general
+iteration waits at its own barrier, then issues its own transfers.  In the
+steady-state loop a barrier serves a pair of iterations (t, t+1): it waits
+for the tiles both blocks read, then issues the transfers of both.
 Transfers of one wave complete in issue order, so "vmcnt(c)" at a barrier
 means: everything this wave issued except its last c transfers has landed.
-These tests replay that schedule for every tile count and buffer count the
-kernel can meet and check, for every wave's transfer counts:
 
-* at each barrier the tiles the iteration reads have landed (the general
-  wait count, and the loop-invariant one of the steady-state loop wherever
-  that loop runs);
-* no transfer is issued into a buffer that an iteration not yet finished
-  still reads.
+These tests replay the schedule for every tile count and buffer count the
+kernel can meet, for every per-wave transfer count, and check that
+
+* at each barrier the tiles the following block(s) read have landed (the
+  general wait count, and the loop-invariant one of the steady-state loop
+  wherever that loop runs);
+* no transfer is issued into a buffer whose previous tile a block at or
+  after that barrier still reads.
 
 No GPU is involved.
 """
@@ -25,88 +30,103 @@ import pytest
 
 
 def issued(j, n, NB, kc, vc):
-    """Transfers a wave with kc K and vc V transfers per tile issues in
+    """Transfers a wave with kc K and vc V transfers per tile issues for
     iteration j (negative j: the prologue)."""
-    vk = j + NB - 2
-    return (kc if j + NB < n else 0) + (vc if 0 <= vk < n else 0)
+    uk, uv = j + NB - 1, j + NB - 3
+    return (kc if 0 <= uk < n else 0) + (vc if 0 <= uv < n else 0)
 
 
-def steady_iterations(n, NB):
-    """Iterations run by the six-way unrolled steady-state loop (NB == 3
-    only): groups t .. t+5 starting at t = 1 while t + 5 + NB < n."""
+def steady_pairs(n, NB):
+    """First iterations of the pairs run by the six-way unrolled steady-state
+    loop (NB == 6): groups t .. t+5 starting at t = 1 while t + 5 + NB < n,
+    pairs starting at t, t+2, t+4."""
     out = set()
-    if NB != 3:
+    if NB != 6:
         return out
     t = 1
     while t + 5 + NB < n:
-        out.update(range(t, t + 6))
+        out.update((t, t + 2, t + 4))
         t += 6
     return out
+
+
+def wait_general(t, n, NB, kc, vc):
+    return sum(issued(j, n, NB, kc, vc) for j in range(t + 3 - NB, t))
+
+
+def wait_pair(t, n, NB, kc, vc):
+    return sum(issued(j, n, NB, kc, vc) for j in range(t + 4 - NB, t))
 
 
 def replay(n, NB, kc, vc):
     seq = []  # (kind, tile) in issue order for this wave
 
-    def issue(kind, u):
-        seq.extend([(kind, u)] * (kc if kind == "K" else vc))
-
     def landed(allowed):
-        """Tiles all of whose transfers have landed when at most `allowed`
-        of this wave's transfers are still in flight."""
         done = seq[:len(seq) - allowed] if allowed else seq
         return {x for x in set(done)
                 if done.count(x) == (kc if x[0] == "K" else vc)}
 
-    # buffer -> (kind, tile) currently held and the last iteration reading it
-    last_read = {}
+    occupant = {}  # buffer -> tile it holds
 
     def reader(kind, u):
-        return u - 1 if kind == "K" else u + 1  # scores of K u in iteration u-1
+        return u - 1 if kind == "K" else u + 1  # the block that reads tile u
 
-    def put(kind, u, t_issue):
+    def put(kind, u, barrier):
+        """Issue tile u at the barrier before block `barrier`."""
         b = (kind, u % NB)
-        if b in last_read:
-            prev = last_read[b]
-            # the previous occupant's last reader must have finished: it ran
-            # in an iteration before t_issue (a barrier sits in between)
-            assert reader(kind, prev) < t_issue, (n, NB, kind, u, prev, t_issue)
-        last_read[b] = u
-        issue(kind, u)
+        if b in occupant:
+            # the previous tile's reader ran before this barrier
+            assert reader(kind, occupant[b]) < barrier, (n, NB, kind, u, occupant[b], barrier)
+        occupant[b] = u
+        seq.extend([(kind, u)] * (kc if kind == "K" else vc))
 
-    for u in range(NB):  # prologue
-        if u < n:
-            put("K", u, u - NB)
-        if u >= 2 and u - 2 < n:
-            put("V", u - 2, u - NB)
-    after = issued(-NB, n, NB, kc, vc) - kc + sum(issued(j, n, NB, kc, vc)
-                                                   for j in range(1 - NB, 0))
+    def issue_iteration(j, barrier):
+        before = len(seq)
+        if 0 <= j + NB - 1 < n:
+            put("K", j + NB - 1, barrier)
+        if 0 <= j + NB - 3 < n:
+            put("V", j + NB - 3, barrier)
+        assert len(seq) - before == issued(j, n, NB, kc, vc)
+
+    for j in range(1 - NB, 0):  # prologue (before block 0)
+        issue_iteration(j, 0)
+    after = issued(1 - NB, n, NB, kc, vc) - kc + sum(issued(j, n, NB, kc, vc)
+                                                      for j in range(2 - NB, 0))
     assert after >= 0
     if kc:
         assert ("K", 0) in landed(after)
-    steady = steady_iterations(n, NB)
-    later_ss = (NB - 2) * (kc + vc)
-    for t in range(n):
-        later = sum(issued(j, n, NB, kc, vc) for j in range(t + 2 - NB, t))
-        if t in steady:
-            assert t + NB < n
-            assert later == later_ss, (n, NB, kc, vc, t)
-        got = landed(later)
-        if t + 1 < n and kc:
-            assert ("K", t + 1) in got, (n, NB, kc, vc, t)
-        if t >= 1 and vc:
-            assert ("V", t - 1) in got, (n, NB, kc, vc, t)
-        before = len(seq)
-        if t + NB < n:
-            put("K", t + NB, t)
-        if t + NB - 2 < n:
-            put("V", t + NB - 2, t)
-        assert len(seq) - before == issued(t, n, NB, kc, vc)
+
+    pairs = steady_pairs(n, NB)
+    ss = (NB - 4) * (kc + vc)  # the steady-state loop's loop-invariant count
+    t = 0
+    while t < n:
+        if t in pairs:
+            assert t + 1 + NB - 1 < n          # every transfer of the pair is issued
+            w = wait_pair(t, n, NB, kc, vc)
+            assert w == ss, (n, NB, kc, vc, t)
+            got = landed(w)
+            for blk in (t, t + 1):
+                if kc and blk + 1 < n:
+                    assert ("K", blk + 1) in got, (n, NB, kc, vc, t, blk)
+                if vc and blk >= 1:
+                    assert ("V", blk - 1) in got, (n, NB, kc, vc, t, blk)
+            issue_iteration(t, t)
+            issue_iteration(t + 1, t)
+            t += 2
+        else:
+            got = landed(wait_general(t, n, NB, kc, vc))
+            if kc and t + 1 < n:
+                assert ("K", t + 1) in got, (n, NB, kc, vc, t)
+            if vc and t >= 1:
+                assert ("V", t - 1) in got, (n, NB, kc, vc, t)
+            issue_iteration(t, t)
+            t += 1
     # the last P.V waits with vmcnt(0): everything has landed
     if vc:
         assert ("V", n - 1) in landed(0)
 
 
-@pytest.mark.parametrize("NB", [3, 4, 5, 6])
+@pytest.mark.parametrize("NB", [4, 5, 6])
 def test_schedule_every_tile_count(NB):
     for n in range(1, 48):
         for kc in range(4):
@@ -115,24 +135,41 @@ def test_schedule_every_tile_count(NB):
 
 
 def test_steady_loop_covers_the_middle():
-    """For long rows the steady-state loop runs all but a few iterations."""
+    """For long rows the steady-state pairs cover all but a few iterations."""
     n = 64
-    s = steady_iterations(n, 3)
-    assert min(s) == 1 and max(s) >= n - 9 and len(s) % 6 == 0
+    p = steady_pairs(n, 6)
+    covered = set()
+    for t in p:
+        covered.update((t, t + 1))
+    assert min(covered) == 1 and max(covered) >= n - 13 and len(covered) % 6 == 0
 
 
 def test_model_catches_a_short_wait():
-    """One transfer more in flight than the kernel allows leaves part of a
-    tile the iteration needs outstanding: the model must see that."""
-    n, NB, kc, vc = 10, 3, 2, 1
+    """One transfer more in flight than the kernel allows at a steady-state
+    pair barrier leaves part of a tile a block needs outstanding."""
+    n, NB, kc, vc = 40, 6, 2, 1
     seq = []
-    for u in range(NB):
-        if u < n:
-            seq.extend([("K", u)] * kc)
-        if u >= 2:
-            seq.extend([("V", u - 2)] * vc)
-    ok = issued(-1, n, NB, kc, vc)  # the kernel's count at iteration 0
-    done_ok = seq[:len(seq) - ok]
-    assert done_ok.count(("K", 1)) == kc
-    done_bad = seq[:len(seq) - (ok + 1)]
-    assert done_bad.count(("K", 1)) < kc
+    for j in range(1 - NB, 7):          # transfers issued before the pair at t = 7
+        for u, kind in ((j + NB - 1, "K"), (j + NB - 3, "V")):
+            if 0 <= u < n:
+                seq.extend([(kind, u)] * (kc if kind == "K" else vc))
+    ok = wait_pair(7, n, NB, kc, vc)
+    assert seq[:len(seq) - ok].count(("K", 9)) == kc
+    assert seq[:len(seq) - (ok + 1)].count(("V", 7)) < vc
+
+
+def test_model_catches_an_early_overwrite():
+    """Issuing the second iteration of a pair into its own K buffer one tile
+    earlier (K tile t+NB instead of t+NB-1 ahead) would overwrite the K tile
+    block t reads: the buffer check must fire."""
+    n, NB = 30, 6
+    occupant = {}
+    reads_k = {t: t + 1 for t in range(n)}
+    bad = False
+    t = 7
+    for j in (t, t + 1):
+        u = j + NB          # one too far
+        b = u % NB
+        if any(reads_k[blk] % NB == b for blk in (t, t + 1)):
+            bad = True
+    assert bad
