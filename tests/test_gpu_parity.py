@@ -452,6 +452,48 @@ def test_streaming_every_row_layout(dev, Lq, Lk, d):
                          f"Lq={Lq} Lk={Lk} d={d} bf16out")
 
 
+@pytest.mark.parametrize("dtype,Lq,Lk,d", [
+    ("bf16", 600, 333, 40), ("bf16", 600, 333, 64), ("f16", 600, 333, 40),
+    ("bf16", 520, 64, 48), ("bf16", 700, 129, 64), ("f16", 600, 1000, 56),
+    ("bf16", 1100, 200, 32)])
+def test_fixed_reference_both_key_orders(dev, dtype, Lq, Lk, d):
+    """Several 256-row query blocks per head: even blocks take the key tiles
+    first to last, odd blocks last to first, so the ragged tile is processed
+    last or first (and supplies the first reference)."""
+    import torch
+    w = Workload("keyorder", "self", 2, 2, Lq, Lk, d, dtype, 13000 + Lq + Lk + d)
+    x = make_inputs(w)
+    want = oracle.attn(x.q, x.k, x.v, w.scale)
+    q, k, v = to_device(x)
+    lo = torch.bfloat16 if dtype == "bf16" else torch.float16
+    say(f"key orders {dtype} Lq={Lq} Lk={Lk} d={d}")
+    assert_bf16_gate(run("stream", q, k, v, w.scale, out_dtype=torch.float32), want,
+                     f"{dtype} Lq={Lq} Lk={Lk} d={d}")
+    assert_bf16_out_gate(run("stream", q, k, v, w.scale, out_dtype=lo), want,
+                         f"{dtype} Lq={Lq} Lk={Lk} d={d} 16-bit out", out=dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [72, 80, 96, 136, 160])
+@pytest.mark.parametrize("Lk", [100, 333, 1024])
+def test_rescaling_key_split(dev, d, Lk, dtype):
+    """Small grids of the rescaling kernel (d > 64): each 32-row query block
+    is shared by four waves on 128-key tiles (head dims up to 96) or two on
+    64-key tiles (wider), whose partial results are merged through LDS;
+    ragged and whole key counts."""
+    import torch
+    w = Workload("ksplit", "self", 2, 2, 100, Lk, d, dtype, 14000 + Lk + d)
+    x = make_inputs(w)
+    want = oracle.attn(x.q, x.k, x.v, w.scale)
+    q, k, v = to_device(x)
+    lo = torch.bfloat16 if dtype == "bf16" else torch.float16
+    say(f"key split {dtype} Lk={Lk} d={d}")
+    assert_bf16_gate(run("stream", q, k, v, w.scale, out_dtype=torch.float32), want,
+                     f"{dtype} Lk={Lk} d={d}")
+    assert_bf16_out_gate(run("stream", q, k, v, w.scale, out_dtype=lo), want,
+                         f"{dtype} Lk={Lk} d={d} 16-bit out", out=dtype)
+
+
 @pytest.mark.parametrize("d", [80, 160])
 def test_rescaling_unsplit_grid(dev, d):
     """d > 64 with enough query blocks for the whole chip: the rescaling

@@ -1,34 +1,43 @@
-// attn_bf16.hip -- bf16 fused attention kernels for gfx950 (MI355X).
+// attn_mfma.hip -- 16-bit (bf16 / fp16) fused attention kernels for gfx950
+// (MI355X).
 //
 // Method: the page "Diffusion inference engine from scratch: Rust + wgpu",
 // section 3.2, computes cross-attention block by block with a running row
 // maximum and running sum so the Q.K^T score matrix never reaches memory.
 // Its WGSL tiles (64 x 64 x 32, 16 x 16 threads, fp32 scores in workgroup
-// memory) target Vulkan/Metal-class GPUs; the design here is CDNA4's own:
+// memory) target Vulkan/Metal-class GPUs; the design here is CDNA4's own.
 //
-// * one wave owns 32 query rows; both products run on the 32x32x16 bf16
-//   matrix cores with fp32 accumulation, in VGPR form (two waves per SIMD,
-//   so no accumulator shuffling through AGPRs);
+// Common to every kernel:
+// * one wave owns 32 query rows; both products run on the 32x32x16
+//   matrix cores (bf16 or fp16 operands, fp32 accumulation), in VGPR form;
 // * scores are produced transposed, S^T = K Q^T, so lane l holds the scores
-//   of query (l % 32) against 16 keys of each 32-key sub-tile: the row
-//   maximum and row sum are in-lane plus one exchange between half-waves;
-// * the S^T accumulator registers, rounded to bf16, are exactly the B
-//   operand of O^T += V^T P^T, so the weights never leave registers; V is
-//   stored transposed in LDS with its keys in the matching order;
-// * the running maximum lives in the log2 domain (exp2 with scale*log2(e)
-//   folded into one FMA) and is raised lazily, only when a sub-tile's maximum
-//   exceeds it by kRescaleSlack binary orders;
-// * when the head dim is padded (d = 40 -> 64, 80 -> 96 rows of V^T), a row
-//   of ones in the padding makes the matrix core produce the row sum l;
-// * K, V and Q are read with range-checked buffer loads: rows past the end
-//   read as zero, and every address is a loop-invariant register plus an
-//   immediate;
-// * streaming kernel: K and V^T tiles of 64 keys double-buffered in LDS,
-//   prefetched into registers one tile ahead, one barrier per tile, the loop
-//   unrolled by two so both LDS buffers have fixed addresses, and the ragged
-//   last tile handled by a separately compiled masked step;
-//   short-key kernel (text contexts, Lk <= 128): all keys loaded to LDS
-//   once, single-pass softmax with no rescaling.
+//   of query (l % 32) against 16 keys of each 32-key sub-tile: row
+//   reductions are in-lane plus one v_permlane32_swap between half-waves;
+// * the S^T accumulator registers, rounded to 16 bits, are exactly the B
+//   operand of O^T += V^T P^T, so the weights never leave registers;
+// * exp2 with scale*log2(e) folded into one FMA; when the head dim is padded
+//   (d = 40 -> 64, 80 -> 96 rows of V^T) a row of ones in the padding makes
+//   the matrix core produce the row sum l;
+// * Q, K and V are read through range-checked buffer descriptors: rows past
+//   the end read as zero;
+// * workgroup ids are renumbered so the query blocks of one head share an
+//   XCD (and its L2 copy of that head's K and V).
+//
+// The kernels:
+// * attn_stream_fix (self-attention, head dims <= 64): eight waves, 64-key
+//   K and V tiles moved by buffer->LDS transfers into six LDS buffers each
+//   (iteration j owns the transfers of K tile j+5 and V tile j+3); each
+//   iteration computes the scores of tile t+1, the weights of tile t and
+//   P.V of tile t-1 in one straight block against a fixed per-row reference
+//   (the first processed tile's maximum; exact fallback on overflow); the
+//   steady-state loop runs one barrier per pair of iterations; odd query
+//   blocks walk the key tiles backwards;
+// * attn_stream_rescale (head dims > 64): lazily rescaled running maximum,
+//   three LDS buffers, and on small grids a two- or four-way split of every
+//   key tile between waves that share a query block, merged through LDS;
+// * attn_short (contexts of up to 128 keys, the text encoder's 77): all keys
+//   resident in LDS, single-pass softmax (the maximum over every key is
+//   known before any exponential), output written through LDS.
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -314,10 +323,17 @@ constexpr int dma_bn() {
   return 3 * 64 * (Shape<DK>::KST + dma_vstr<DK>()) * 2 <= 160 * 1024 ? 64 : 32;
 }
 
-template <int DK, int NW>
+// 128-key tiles (for the four-way key split) when three K and three V
+// buffers of that size fit in the CU's 160 KB.
+template <int DK>
+constexpr bool dma_fits_128() {
+  return 3 * 128 * (Shape<DK>::KST + dma_vstr<DK>()) * 2 <= 160 * 1024;
+}
+
+template <int DK, int NW, int BN_ = dma_bn<DK>()>
 struct DmaPlan {
   using S = Shape<DK>;
-  static constexpr int BN = dma_bn<DK>();
+  static constexpr int BN = BN_;
   static constexpr int NSUB = BN / 32;
   static constexpr int NB = 3;                      // LDS buffers per operand
   static constexpr int KCR = S::KST / 8;            // 16-byte chunks per K row
@@ -331,23 +347,24 @@ struct DmaPlan {
   static constexpr int NIW = (NI + NW - 1) / NW;    // per wave, upper bound
 };
 
-// KS = 2 splits every 64-key tile between two waves that own the same 32
-// query rows (each takes one 32-key sub-tile): a workgroup then covers
-// NW/2 query blocks, so small problems launch twice as many waves.  Each wave
-// keeps its own running maximum, row sum and O over its keys; the two
-// partial results are merged through LDS at the end (O = a0*O0 + a1*O1,
-// l = a0*l0 + a1*l1 with a_w = 2^(m_w - max(m0, m1))).
+// KS = 2 (4) splits every 64-key (128-key) tile between KS waves that own
+// the same 32 query rows, each taking one 32-key sub-tile: a workgroup then
+// covers NW/KS query blocks, so small problems launch KS times as many
+// waves.  Each wave keeps its own running maximum, row sum and O over its
+// keys; the partial results are merged through LDS at the end
+// (O = sum_w a_w O_w, l = sum_w a_w l_w, a_w = 2^(m_w - max_w m_w)).
 template <int DK, int NW, bool OUT_F32, bool H, int KS = 1>
 __global__ __launch_bounds__(NW * kWave, (waves_per_simd<DK>()))
 void attn_stream_rescale(Args16 a) {
   using S = Shape<DK>;
-  using P = DmaPlan<DK, NW>;
+  using P = DmaPlan<DK, NW, (KS == 4 ? 128 : dma_bn<DK>())>;
   constexpr int BN = P::BN, NSUB = P::NSUB;
-  static_assert(KS == 1 || (KS == 2 && NSUB == 2 && NW % 2 == 0), "two-way split of 64-key tiles");
+  static_assert(KS == 1 || (KS == NSUB && NW % KS == 0), "one 32-key sub-tile per wave and tile");
   // merge area of the split form: per wave pair, O^T (MT x 16 floats per
   // lane), then m and l (one float per lane each)
   constexpr int kMergeFloats = S::MT * 16 * 64 + 2 * 64;
-  static_assert(KS == 1 || (NW / 2) * kMergeFloats * 4 <= P::NB * (P::KBUF + P::VBUF) * 2,
+  static_assert(KS == 1 || (NW / KS) * (KS - 1) * kMergeFloats * 4 <=
+                               P::NB * (P::KBUF + P::VBUF) * 2,
                 "merge area fits in the tile buffers");
   __shared__ __attribute__((aligned(16))) uint16_t smem[P::NB * (P::KBUF + P::VBUF)];
   uint16_t *const Ks = smem;
@@ -505,7 +522,7 @@ void attn_stream_rescale(Args16 a) {
     if (t + 2 < ntiles) issue(t + 2, (B + 2) % 3);
     const uint16_t *kb = Ks + B * P::KBUF + koff;
     const uint16_t *vb = Vs + B * P::VBUF;
-    if constexpr (KS == 2) {
+    if constexpr (KS > 1) {
       f32x16 s0 = scores_subtile<DK, H>(kb + 32 * kh * S::KST, qf);
       sub(mask_c, s0, t * BN + 32 * kh, vb, 2 * kh);
     } else {
@@ -540,35 +557,46 @@ void attn_stream_rescale(Args16 a) {
     step(B0{}, Ragged{}, t);
   }
 
-  if constexpr (KS == 2) {
+  if constexpr (KS > 1) {
     // Every wave is done with the tile buffers (no transfer is in flight
-    // after the last tile); they now hold the second wave's partial result.
-    float *const mg = reinterpret_cast<float *>(smem) + qw * kMergeFloats;
+    // after the last tile); they now hold the other waves' partial results,
+    // KS-1 slots per query block.
+    float *const mg = reinterpret_cast<float *>(smem) + qw * (KS - 1) * kMergeFloats;
     const float lw = S::kOnes ? 0.f : sum_halves(lsum);
     __syncthreads();
-    if (kh == 1) {
+    if (kh > 0) {
+      float *const slot = mg + (kh - 1) * kMergeFloats;
 #pragma unroll
       for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mg[(mt * 16 + i) * 64 + lane] = o[mt][i];
-      mg[S::MT * 16 * 64 + lane] = m_run;
-      mg[S::MT * 16 * 64 + 64 + lane] = lw;
+        for (int i = 0; i < 16; ++i) slot[(mt * 16 + i) * 64 + lane] = o[mt][i];
+      slot[S::MT * 16 * 64 + lane] = m_run;
+      slot[S::MT * 16 * 64 + 64 + lane] = lw;
     }
     __syncthreads();
     if (kh == 0) {
-      // key 0 is in this wave's half, so m_run is finite; the other half may
+      // key 0 is in this wave's part, so m_run is finite; another part may
       // have seen no key (m = -inf, O = 0, l = 0): its factor is then 0
-      const float m1 = mg[S::MT * 16 * 64 + lane];
-      const float mx = fmaxf(m_run, m1);
-      const float a0 = fast_exp2(m_run - mx), a1 = fast_exp2(m1 - mx);
+      float mx = m_run;
 #pragma unroll
-      for (int mt = 0; mt < S::MT; ++mt)
+      for (int w = 1; w < KS; ++w) mx = fmaxf(mx, mg[(w - 1) * kMergeFloats + S::MT * 16 * 64 + lane]);
+      const float a0 = fast_exp2(m_run - mx);
+      float l = a0 * lw;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[mt][i] = a0 * o[mt][i] + a1 * mg[(mt * 16 + i) * 64 + lane];
+      for (int mt = 0; mt < S::MT; ++mt) o[mt] *= a0;
+#pragma unroll
+      for (int w = 1; w < KS; ++w) {
+        const float *slot = mg + (w - 1) * kMergeFloats;
+        const float aw = fast_exp2(slot[S::MT * 16 * 64 + lane] - mx);
+#pragma unroll
+        for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[mt][i] += aw * slot[(mt * 16 + i) * 64 + lane];
+        l += aw * slot[S::MT * 16 * 64 + 64 + lane];
+      }
       if constexpr (S::kOnes) {
         store_out<DK, OUT_F32, H>(o, 0.f, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
       } else {
-        const float l = a0 * lw + a1 * mg[S::MT * 16 * 64 + 64 + lane];
         store_out_l<DK, OUT_F32, H>(o, l, a.out, a.lo.head(bh, a.H), q0, Lq, d, a.lo.sl, lane);
       }
     }
@@ -675,10 +703,12 @@ __device__ __forceinline__ float rows_exact(f32x16 (&o)[Shape<DK>::MT],
   return sum_halves(lsum);
 }
 
-// LDS buffers per operand in the fixed-reference kernel: K tiles are
-// requested NB iterations ahead, V tiles NB-2 ahead (3 measured best).
+// LDS buffers per operand in the fixed-reference kernel: iteration j owns
+// the transfers of K tile j+NB-1 and V tile j+NB-3; the steady-state loop
+// runs one barrier per pair of iterations, which needs NB >= 4 (6: the
+// transfers of a pair have a pair's time in flight before they are needed).
 #ifndef SDATTN_FIX_BUFFERS
-#define SDATTN_FIX_BUFFERS 3
+#define SDATTN_FIX_BUFFERS 6
 #endif
 constexpr int kFixBuffers = SDATTN_FIX_BUFFERS;
 template <int V>
@@ -727,7 +757,7 @@ void attn_stream_fix(Args16 a) {
   using P = FixPlan<DK, D, NW>;
   constexpr int BN = P::BN;
   constexpr int NB = kFixBuffers;  // LDS buffers per operand
-  static_assert(NB >= 3, "K runs NB tiles ahead, V NB-2 tiles ahead");
+  static_assert(NB == 6, "the steady-state loop folds six buffer phases");
   __shared__ __attribute__((aligned(16))) uint16_t
       smem[NB * (P::KBUF + P::VBUF) + (P::VTAIL + 7) / 8 * 8];
   uint16_t *const Ks = smem;
@@ -750,11 +780,22 @@ void attn_stream_fix(Args16 a) {
   const u32x4 kw = rsrc_words(kbase, kvbytes), vw = rsrc_words(vbase, kvbytes);
   const int n = (Lk + BN - 1) / BN;
   const bool ragged = (Lk % BN) != 0;
+  // Odd query blocks walk the key tiles from the last one down.  When a
+  // head has more query blocks than one round of its XCD's CUs takes (the
+  // 128x128 latent: 64 blocks, 32 CUs), the next round then starts on the
+  // tiles the previous one read last, still in L2, instead of re-reading
+  // from HBM the ones it read first (evicted: a head's K and V outgrow the
+  // 4 MB L2).  Any tile order gives the same result.  key_tile(j): the key
+  // tile processed j-th; the ragged tile is processed first or last.
+  const bool rev = ((wg - bh * a.qblocks) & 1) != 0;
+  auto key_tile = [&](int j) { return rev ? n - 1 - j : j; };
+  const bool ragged_first = ragged && rev && n > 1, ragged_last = ragged && !rev;
 
   // Transfers: instruction i = wave + NW*r covers 64 consecutive 16-byte
   // chunks of a K (i < KI) or V buffer.  K tile u goes to K buffer u % NB and
-  // V tile u to V buffer u % NB; iteration j starts K tile j+NB and V tile
-  // j+NB-2 (the prologue plays iterations -NB .. -1).
+  // V tile u to V buffer u % NB; iteration j owns K tile j+NB-1 and V tile
+  // j+NB-3 (the prologue plays iterations 1-NB .. -1).  Iteration t reads K
+  // tile t+1 and V tile t-1; both are owned by iteration t+2-NB.
   uint32_t goff[P::NIW];
   uint32_t loff[P::NIW];  // byte offset within a buffer
   bool isk[P::NIW], act[P::NIW];
@@ -778,44 +819,64 @@ void attn_stream_fix(Args16 a) {
     if (wave + NW * r < P::NI && __any(act[r])) {
       if (isk[r]) ++kc; else ++vc;
     }
+  // Which of its NIW slots this wave issues as a K or a V transfer, and each
+  // slot's LDS byte offset within a buffer: wave-uniform values, taken into
+  // scalar registers once so the issue code below is scalar arithmetic and
+  // scalar branches (with per-lane conditions the compiler kept them as
+  // lane masks and rebuilt each branch condition through vector
+  // instructions, ~165 cycles per tile).
+  int kon[P::NIW], von[P::NIW];
+  uint32_t lofs[P::NIW];
+#pragma unroll
+  for (int r = 0; r < P::NIW; ++r) {
+    const bool on = wave + NW * r < P::NI;
+    kon[r] = __builtin_amdgcn_readfirstlane((on && isk[r]) ? 1 : 0);
+    von[r] = __builtin_amdgcn_readfirstlane((on && !isk[r]) ? 1 : 0);
+    lofs[r] = __builtin_amdgcn_readfirstlane(loff[r]);
+  }
   const uint32_t ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
   auto issue_k = [&](int tt, int b) {
-    const uint32_t toff = (uint32_t)(tt * BN * slk) * 2u;
+    const uint32_t toff = (uint32_t)(key_tile(tt) * BN * slk) * 2u;
     const uint32_t dst = ks_lds + (uint32_t)(b * P::KBUF) * 2u;
 #pragma unroll
     for (int r = 0; r < P::NIW; ++r)
-      if (wave + NW * r < P::NI && isk[r]) {
-        // wave-uniform; readfirstlane keeps it in a scalar register where
-        // the compiler would otherwise leave it in a vector one
-        const uint32_t l = __builtin_amdgcn_readfirstlane(dst + loff[r]);
+      if (kon[r]) {
+        // readfirstlane: a no-op on a value already in a scalar register,
+        // and a guarantee where the compiler would leave it in a vector one
+        const uint32_t l = __builtin_amdgcn_readfirstlane(dst + lofs[r]);
         if constexpr (P::KFULL) dma16_raw(kw, toff + goff[r], l);
         else if (act[r]) dma16_raw(kw, toff + goff[r], l);
       }
   };
   auto issue_v = [&](int tt, int b) {
-    const uint32_t toff = (uint32_t)(tt * BN * slk) * 2u;
+    const uint32_t toff = (uint32_t)(key_tile(tt) * BN * slk) * 2u;
     const uint32_t dst = vs_lds + (uint32_t)(b * P::VBUF) * 2u;
 #pragma unroll
     for (int r = 0; r < P::NIW; ++r)
-      if (wave + NW * r < P::NI && !isk[r]) {
-        const uint32_t l = __builtin_amdgcn_readfirstlane(dst + loff[r]);
+      if (von[r]) {
+        const uint32_t l = __builtin_amdgcn_readfirstlane(dst + lofs[r]);
         if (act[r]) dma16_raw(vw, toff + goff[r], l);
       }
   };
 
-  // Transfers this wave issues in iteration j (prologue included).
+  // Transfers this wave issues for iteration j (prologue included), and
+  // iteration j's transfers themselves (the buffer of K tile j+NB-1 held K
+  // tile j-1, read in iteration j-2; that of V tile j+NB-3 held V tile j-3,
+  // read in iteration j-2).
   auto issued = [&](int j) {
-    const int vk = j + NB - 2;
-    return (j + NB < n ? kc : 0) + (vk >= 0 && vk < n ? vc : 0);
+    const int uk = j + NB - 1, uv = j + NB - 3;
+    return (uk >= 0 && uk < n ? kc : 0) + (uv >= 0 && uv < n ? vc : 0);
+  };
+  auto issue_iter = [&](int j) {
+    const int uk = j + NB - 1, uv = j + NB - 3;
+    if (uk >= 0 && uk < n) issue_k(uk, uk % NB);
+    if (uv >= 0 && uv < n) issue_v(uv, uv % NB);
   };
 
   bf16x8 qf[DK / 16];
   load_q<DK>(qf, qr, q0, d, slq, a.qsign, lane);
 #pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    if (u < n) issue_k(u, u);
-    if (u >= 2 && u - 2 < n) issue_v(u - 2, u - 2);
-  }
+  for (int j = 1 - NB; j < 0; ++j) issue_iter(j);
 
   // Constants the transfers never write: the zero chunk after each K buffer
   // and the V chunk at column D (a one at D, zeros after it).
@@ -865,9 +926,9 @@ void attn_stream_fix(Args16 a) {
   // Tile 0's K has landed (everything the prologue issued after it may be
   // in flight): scores and the reference of every row.
   {
-    int after = issued(-NB) - kc;
+    int after = issued(1 - NB) - kc;
 #pragma unroll
-    for (int j = 1 - NB; j < 0; ++j) after += issued(j);
+    for (int j = 2 - NB; j < 0; ++j) after += issued(j);
     vmcnt_barrier_rt<NB * P::NIW>(after);
   }
   f32x16 sA0, sA1, sB0, sB1;
@@ -875,11 +936,12 @@ void attn_stream_fix(Args16 a) {
   float nm;
   {
     f32x16 m0 = sA0, m1 = sA1;
-    if (n == 1 && ragged) {
+    if ((n == 1 && ragged) || ragged_first) {
+      const int key0 = key_tile(0) * BN;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (acc_key(i, lane) >= Lk) m0[i] = -__builtin_inff();
-        if (32 + acc_key(i, lane) >= Lk) m1[i] = -__builtin_inff();
+        if (key0 + acc_key(i, lane) >= Lk) m0[i] = -__builtin_inff();
+        if (key0 + 32 + acc_key(i, lane) >= Lk) m1[i] = -__builtin_inff();
       }
     }
     nm = -(max_halves(max16(m1, max16(m0, -__builtin_inff()))) * c);
@@ -908,45 +970,50 @@ void attn_stream_fix(Args16 a) {
       }
   };
 
-  // Iteration t: wait for K tile t+1 and V tile t-1 (both started in
-  // iteration t+1-NB; later ones may stay in flight), start K t+NB and
-  // V t+NB-2 into the buffers read in iteration t-1, then -- one block of independent
-  // work -- scores of tile t+1 (into nx), weights of tile t (from cu, into
-  // pout) and P.V of tile t-1 (weights pin).  Alternate register roles
-  // between consecutive iterations avoid copies.
-  // Transfers still allowed in flight at a steady-state barrier (every
-  // iteration in between issues all of its K and V transfers).
-  const int later_ss = __builtin_amdgcn_readfirstlane((NB - 2) * (kc + vc));
+  // Iteration t: wait for K tile t+1 and V tile t-1 (owned by iteration
+  // t+2-NB; later ones may stay in flight), issue iteration t's transfers,
+  // then -- one block of independent work -- scores of tile t+1 (into nx),
+  // weights of tile t (from cu, into pout) and P.V of tile t-1 (weights
+  // pin).  Alternate register roles between consecutive iterations avoid
+  // copies.
+  // Steady state: one barrier per pair (t, t+1), t odd.  It waits for the
+  // tiles of both blocks (owned by iterations up to t+3-NB; the transfers of
+  // the previous pair may stay in flight: later_ss) and issues the transfers
+  // of both iterations (their buffers are read by neither block, NB >= 4);
+  // the pair's second block runs straight on.  Half the barriers and
+  // transfer-issue points of one per iteration (measured: those took ~28 %
+  // of an iteration's cycles on the 64x64-latent workload).
+  const int later_ss = __builtin_amdgcn_readfirstlane((NB - 4) * (kc + vc));
   // PH_c: -1 for the general iteration; else the steady-state form with
-  // t % NB == PH (buffer numbers fold to constants) and t + NB < n (every
-  // transfer is issued, the wait count is later_ss): far fewer scalar
-  // instructions per iteration.
+  // t % NB == PH (buffer numbers fold to constants; odd PH: first of a
+  // pair, even PH: second) and every transfer of the pair issued (the wait
+  // count is later_ss): far fewer scalar instructions per iteration.
   auto body = [&](auto pv_c, auto next_c, auto mask_c, auto ph_c, int t, const f32x16 &cu0,
                   const f32x16 &cu1, f32x16 &nx0, f32x16 &nx1, const u32x4 (&pin)[4],
                   u32x4 (&pout)[4]) {
     constexpr bool HAS_PV = decltype(pv_c)::value;
     constexpr bool HAS_NEXT = decltype(next_c)::value;
     constexpr int PH = decltype(ph_c)::value;
-    int b, b1, b2, bv;
+    int b1, b2;  // K buffer read by the scores, V buffer read by P.V
     if constexpr (PH >= 0) {
-      vmcnt_barrier_rt<(NB - 2) * P::NIW>(later_ss);
-      b = PH;
+      if constexpr (PH % 2 == 1) {
+        vmcnt_barrier_rt<(NB - 4) * P::NIW>(later_ss);
+        issue_k(t + NB - 1, (PH + NB - 1) % NB);
+        issue_v(t + NB - 3, (PH + NB - 3) % NB);
+        issue_k(t + NB, PH);
+        issue_v(t + NB - 2, (PH + NB - 2) % NB);
+      }
       b1 = (PH + 1) % NB;
       b2 = (PH + NB - 1) % NB;
-      bv = (PH + NB - 2) % NB;
-      issue_k(t + NB, b);
-      issue_v(t + NB - 2, bv);
     } else {
       int later = 0;
 #pragma unroll
-      for (int j = t + 2 - NB; j < t; ++j) later += issued(j);
-      vmcnt_barrier_rt<(NB - 2) * P::NIW>(later);
-      b = t % NB;
+      for (int j = t + 3 - NB; j < t; ++j) later += issued(j);
+      vmcnt_barrier_rt<(NB - 3) * P::NIW>(later);
+      const int b = t % NB;
       b1 = b == NB - 1 ? 0 : b + 1;
       b2 = b == 0 ? NB - 1 : b - 1;
-      bv = b >= 2 ? b - 2 : b + NB - 2;
-      if (t + NB < n) issue_k(t + NB, b);
-      if (t + NB - 2 < n) issue_v(t + NB - 2, bv);
+      issue_iter(t);
     }
     // fp16 weights must stay below fp16's largest value: when a row's tile
     // maximum rises more than kRescaleSlack above the reference, the
@@ -959,8 +1026,8 @@ void attn_stream_fix(Args16 a) {
       if constexpr (decltype(mask_c)::value) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          if (t * BN + acc_key(i, lane) >= Lk) m0[i] = -__builtin_inff();
-          if (t * BN + 32 + acc_key(i, lane) >= Lk) m1[i] = -__builtin_inff();
+          if (key_tile(t) * BN + acc_key(i, lane) >= Lk) m0[i] = -__builtin_inff();
+          if (key_tile(t) * BN + 32 + acc_key(i, lane) >= Lk) m1[i] = -__builtin_inff();
         }
       }
       const float tmax = max_halves(max16(m1, max16(m0, -__builtin_inff()))) * c;
@@ -980,7 +1047,7 @@ void attn_stream_fix(Args16 a) {
     // MFMAs of this block (measured 1-3 % faster than its default order).
     __builtin_amdgcn_iglp_opt(0);
     if constexpr (HAS_NEXT) scores(b1, nx0, nx1);
-    weights(mask_c, t * BN, cu0, cu1, nmt, pout);
+    weights(mask_c, key_tile(t) * BN, cu0, cu1, nmt, pout);
     if constexpr (HAS_PV) pv(b2, pin);
     if constexpr (H) {
       if (resc) {
@@ -1004,7 +1071,7 @@ void attn_stream_fix(Args16 a) {
   // Last iteration (no next tile) and the P.V of the last tile.
   auto finish = [&](int t, const f32x16 &cu0, const f32x16 &cu1, const u32x4 (&pin)[4],
                     u32x4 (&pout)[4]) {
-    if (ragged) body(T{}, F{}, T{}, G{}, t, cu0, cu1, sA0, sA1, pin, pout);
+    if (ragged_last) body(T{}, F{}, T{}, G{}, t, cu0, cu1, sA0, sA1, pin, pout);
     else body(T{}, F{}, F{}, G{}, t, cu0, cu1, sA0, sA1, pin, pout);
     vmcnt_barrier<0>();
     pv(t % NB, pout);
@@ -1016,17 +1083,18 @@ void attn_stream_fix(Args16 a) {
     vmcnt_barrier<0>();
     pv(0, pA);
   } else {
-    body(F{}, T{}, F{}, G{}, 0, sA0, sA1, sB0, sB1, pB, pA);
+    if (ragged_first) body(F{}, T{}, T{}, G{}, 0, sA0, sA1, sB0, sB1, pB, pA);
+    else body(F{}, T{}, F{}, G{}, 0, sA0, sA1, sB0, sB1, pB, pA);
     int t = 1;
-    if constexpr (NB == 3) {
-      // Steady state: six iterations run both register roles through all
-      // three buffer phases (t = 1 mod 6 on entry, as t % 3 == 1 and t odd).
+    {
+      // Steady state: six iterations (three pairs) run both register roles
+      // through all six buffer phases (t = 1 mod 6 on entry).
       for (; t + 5 + NB < n; t += 6) {
         body(T{}, T{}, F{}, IntC<1>{}, t, sB0, sB1, sA0, sA1, pA, pB);
         body(T{}, T{}, F{}, IntC<2>{}, t + 1, sA0, sA1, sB0, sB1, pB, pA);
-        body(T{}, T{}, F{}, IntC<0>{}, t + 2, sB0, sB1, sA0, sA1, pA, pB);
-        body(T{}, T{}, F{}, IntC<1>{}, t + 3, sA0, sA1, sB0, sB1, pB, pA);
-        body(T{}, T{}, F{}, IntC<2>{}, t + 4, sB0, sB1, sA0, sA1, pA, pB);
+        body(T{}, T{}, F{}, IntC<3>{}, t + 2, sB0, sB1, sA0, sA1, pA, pB);
+        body(T{}, T{}, F{}, IntC<4>{}, t + 3, sA0, sA1, sB0, sB1, pB, pA);
+        body(T{}, T{}, F{}, IntC<5>{}, t + 4, sB0, sB1, sA0, sA1, pA, pB);
         body(T{}, T{}, F{}, IntC<0>{}, t + 5, sA0, sA1, sB0, sB1, pB, pA);
       }
     }
@@ -1295,6 +1363,12 @@ constexpr int kStreamWaves = SDATTN_STREAM_WAVES;          // rescaling streamin
 #define SDATTN_SPLIT_BELOW 256
 #endif
 constexpr int kSplitBelow = SDATTN_SPLIT_BELOW;
+// Below this many workgroups of the two-way split, four waves share each
+// query block (head dims whose 128-key tiles fit three times in LDS).
+#ifndef SDATTN_SPLIT4_BELOW
+#define SDATTN_SPLIT4_BELOW 512
+#endif
+constexpr int kSplit4Below = SDATTN_SPLIT4_BELOW;
 constexpr int kShortWaves = SDATTN_SHORT_WAVES;
 constexpr int kShortTiles = SDATTN_SHORT_TILES;   // query tiles per wave (short kernel)
 // Below this many four-wave workgroups the short kernel runs two-wave ones.
@@ -1335,9 +1409,25 @@ hipError_t launch_rescale(Args16 a, int BH, bool out_f32, hipStream_t stream) {
   const dim3 block(NW * kWave);
   if constexpr (DmaPlan<DK, NW>::NSUB == 2) {
     if (a.nwg < kSplitBelow) {
-      // few workgroups for the chip: two waves share each query block
+      // few workgroups for the chip: two waves share each query block, or
+      // four (one per SIMD, on 128-key tiles) when that still leaves fewer
+      // than two waves per SIMD on the chip
+      const int nwg2 = BH * ((a.Lq + NW / 2 * kQW - 1) / (NW / 2 * kQW));
+      if constexpr (dma_fits_128<DK>()) {
+        if (nwg2 < kSplit4Below) {
+          // eight-wave workgroups (two query blocks x four key parts): the
+          // 128-key tiles leave room for one workgroup per CU
+          constexpr int NW8 = 8;
+          a.qblocks = (a.Lq + NW8 / 4 * kQW - 1) / (NW8 / 4 * kQW);
+          a.nwg = BH * a.qblocks;
+          const dim3 grid(a.nwg), block8(NW8 * kWave);
+          return out_f32
+                     ? launch_kernel(&attn_stream_rescale<DK, NW8, true, H, 4>, grid, block8, 0, stream, a)
+                     : launch_kernel(&attn_stream_rescale<DK, NW8, false, H, 4>, grid, block8, 0, stream, a);
+        }
+      }
       a.qblocks = (a.Lq + NW / 2 * kQW - 1) / (NW / 2 * kQW);
-      a.nwg = BH * a.qblocks;
+      a.nwg = nwg2;
       const dim3 grid(a.nwg);
       return out_f32
                  ? launch_kernel(&attn_stream_rescale<DK, NW, true, H, 2>, grid, block, 0, stream, a)
