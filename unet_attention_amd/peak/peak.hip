@@ -120,9 +120,61 @@ __global__ __launch_bounds__(256) void k_lds(LdsArgs a) {
   a.sink[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
 }
 
+// One wave: the lane layouts the attention kernels rely on, written out for
+// a test to compare with their documented form.
+//  out[0 .. 1023]: v_mfma_f32_32x32x16_bf16 with A[r][k] = (k == r % 16) and
+//    B[k][c] = k, the operands placed as documented (lane l supplies row /
+//    column l % 32 and k = 8 (l / 32) .. +7): accumulator register i of lane
+//    l, written at 16 l + i, must read (8 (i / 4) + 4 (l / 32) + i % 4) % 16;
+//  out[1024 .. 2047]: the same with A[r][k] = (k == 0) and B[k][c] = c % 32:
+//    register i of lane l must read l % 32;
+//  out[2048 .. 2303]: ds_read_b64_tr_b16 from an LDS table holding value x
+//    at halfword x, each lane addressing halfword 4 l: the four halfwords
+//    lane l receives, at 4 l + j;
+//  out[2304 .. 2431]: v_permlane32_swap with both operands 100 + l (the
+//    form the kernels use): both results of each lane.
+__global__ __launch_bounds__(64) void k_probe(int *out) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  __shared__ __attribute__((aligned(16))) uint16_t tab[512];
+  const int l = threadIdx.x;
+  for (int i = l; i < 512; i += 64) tab[i] = (uint16_t)i;
+  __syncthreads();
+  const int r = l % 32, kb = 8 * (l / 32);
+  bf16x8 a1, b1, a2, b2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = kb + j;
+    a1[j] = (__bf16)(k == r % 16 ? 1.0f : 0.0f);
+    b1[j] = (__bf16)(float)k;
+    a2[j] = (__bf16)(k == 0 ? 1.0f : 0.0f);
+    b2[j] = (__bf16)(float)(l % 32);
+  }
+  const f32x16 d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, f32x16{}, 0, 0, 0);
+  const f32x16 d2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b2, f32x16{}, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    out[16 * l + i] = (int)d1[i];
+    out[1024 + 16 * l + i] = (int)d2[i];
+  }
+  const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tab + 4 * l));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[2048 + 4 * l + j] = (int)(uint16_t)t[j];
+  const auto sw = __builtin_amdgcn_permlane32_swap((uint32_t)(100 + l), (uint32_t)(100 + l), false,
+                                                   false);
+  out[2304 + 2 * l] = (int)sw[0];
+  out[2304 + 2 * l + 1] = (int)sw[1];
+}
+
 }  // namespace
 
 extern "C" {
+
+// Writes the 2432 ints described at k_probe to out (device memory).
+int peak_probe_layouts(int *out, void *stream) {
+  return (int)launch1(&k_probe, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), out);
+}
+
 
 // n_exp in {0, 2, 4, 8}, n_fma in {0, 4, 8}; sink holds nwg * 256 floats.
 int peak_mfma(int nwg, int iters, int n_exp, int n_fma, float *sink, void *stream) {
