@@ -549,6 +549,19 @@ def cpu_baseline(args, calls, ws, inputs, set0, step_flops):
                 single[n] = {"value": round(w.flops / t1 / 1e12, 6), "unit": "TFLOP/s",
                              "seconds": round(t1, 3)}
         worst[n] = {"max_abs": float(e.max()), "mean_abs": float(e.mean())}
+    # one thread on the smaller workloads of the pages' UNet levels as well
+    # (cheap: ~1 s in all), for the single-core rate at those shapes
+    for n in ("1", "3", "4a", "4b", "4c", "4d"):
+        if n in single or n in [c for c, _ in calls]:
+            continue
+        w = WORKLOADS[n]
+        x = make_inputs(w)
+        q, k, v = (np.ascontiguousarray(a, dtype=np.float64) for a in (x.q, x.k, x.v))
+        t0 = time.perf_counter()
+        orc.attn(q, k, v, w.scale, nthreads=1)
+        t1 = time.perf_counter() - t0
+        single[n] = {"value": round(w.flops / t1 / 1e12, 6), "unit": "TFLOP/s",
+                     "seconds": round(t1, 3)}
     cpu = {"value": round(flops_done / total / 1e12, 6), "unit": "TFLOP/s",
            "cores": threads, "kind": "oracle",
            "sample": f"{'; '.join(samples)}; fp64, {total:.2f} s on {threads} threads of "

@@ -78,8 +78,9 @@ typedef enum {
 
 /* Attention with any key length.  Internally dispatches to the short-key
  * kernel (all keys resident in LDS, single-pass softmax) when
- * Lk <= sdattn_cross_max_ctx(d, dtype), and to the streaming kernel
- * (K/V tiles double-buffered through LDS, online softmax) otherwise.
+ * Lk <= sdattn_cross_max_ctx(d, dtype), and to a streaming kernel
+ * (K/V tiles streamed through several LDS buffers ahead of their use,
+ * blockwise softmax) otherwise.
  * Used for UNet self-attention (Lk = Lq = HW). */
 int sdattn_fwd(const void *q, const void *k, const void *v, void *out, int B,
                int H, int Lq, int Lk, int d, float scale, int dtype,
