@@ -245,7 +245,10 @@ def attainable_peaks(torch, stream, copy_bytes):
     lib.peak_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     sh = stream.cuda_stream
 
-    def timed(launch, reps):
+    seq = []  # (label, launches, work per launch) in launch order, for profilers
+
+    def timed(launch, reps, label, work):
+        seq.append([label, reps + 1, work])
         launch()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -266,7 +269,7 @@ def attainable_peaks(torch, stream, copy_bytes):
             rc = lib.peak_mfma(nwg, iters, ne, nf, sink.data_ptr(), sh)
             if rc:
                 raise RuntimeError(f"peak_mfma failed ({rc})")
-        mf[f"exp{ne}_fma{nf}"] = round(flops / timed(go, 3) / 1e12, 1)
+        mf[f"exp{ne}_fma{nf}"] = round(flops / timed(go, 3, f"mfma exp{ne}_fma{nf}", flops) / 1e12, 1)
     out["mfma_bf16_tflops"] = mf.pop("exp0_fma0")
     out["mfma_bf16_tflops_with_vector_work_per_mfma"] = mf
     # copies: copy_bytes of traffic (half read, half written), rotated
@@ -284,7 +287,7 @@ def attainable_peaks(torch, stream, copy_bytes):
         rc = lib.peak_copy(a_.data_ptr(), b_.data_ptr(), half, 1024, sh)
         if rc:
             raise RuntimeError(f"peak_copy failed ({rc})")
-    t_small = timed(cp, 4 * nbuf)
+    t_small = timed(cp, 4 * nbuf, f"copy {2 * half} bytes", 2 * half)
     out["copy"] = {f"{2 * half / 1e6:.2f}MB_us": round(t_small * 1e6, 2),
                    f"{2 * half / 1e6:.2f}MB_gbs": round(2 * half / t_small / 1e9, 1)}
     del bufs
@@ -292,16 +295,19 @@ def attainable_peaks(torch, stream, copy_bytes):
     a_ = torch.empty(big, dtype=torch.uint8, device="cuda")
     b_ = torch.empty(big, dtype=torch.uint8, device="cuda")
     a_.fill_(1)
-    t_big = timed(lambda: lib.peak_copy(a_.data_ptr(), b_.data_ptr(), big, 8192, sh), 5)
+    t_big = timed(lambda: lib.peak_copy(a_.data_ptr(), b_.data_ptr(), big, 8192, sh), 5,
+                  f"copy {2 * big} bytes", 2 * big)
     out["copy"]["1GiB_gbs"] = round(2 * big / t_big / 1e9, 1)
     del a_, b_
     lnwg, liters = 1024, 4000
     lsink = torch.empty(lnwg * 256, dtype=torch.float32, device="cuda")
-    t_lds = timed(lambda: lib.peak_lds(lnwg, liters, lsink.data_ptr(), sh), 3)
+    t_lds = timed(lambda: lib.peak_lds(lnwg, liters, lsink.data_ptr(), sh), 3,
+                  "lds b128 reads", lnwg * 256 * liters * 8 * 16)
     out["lds_read_gbs"] = round(lnwg * 256 * liters * 8 * 16 / t_lds / 1e9, 1)
     out["method"] = ("HIP events around back-to-back launches; MFMA: 512 workgroups of 4 waves, "
                      "v_mfma_f32_32x32x16_bf16 on 4 accumulators per wave; copies with 16-byte "
                      "lanes")
+    out["_sequence"] = seq
     return out
 
 
@@ -340,6 +346,11 @@ def suite(args, torch, sd):
         print(json.dumps({"suite_row": f"gn_{name}", "launches_per_call": args.warmup + args.steps,
                           "warmup": args.warmup, "calls": [f"group_norm {name}"],
                           "kernel_source_sha": kernel_source_sha()}), flush=True)
+    # attainable-peak microbenchmarks (libsdattn_peak.so), copy sized like the
+    # cross-attention call of the default step
+    peaks = attainable_peaks(torch, stream, WORKLOADS["3"].bytes_alg(2))
+    seq = peaks.pop("_sequence", [])
+    print(json.dumps({"suite_row": "peaks", "sequence": seq, "event_timed": peaks}), flush=True)
 
 
 def main():
@@ -420,6 +431,19 @@ def main():
     step_flops = sum(w.flops for w in ws)
     value = step_flops / (ms_step * 1e-3) / 1e12
     prof = load_kernel_profile(args.workload) or {}
+    # Some boards report an idle-level GFX clock while busy.  The dense bf16
+    # peak is 2.5 PFLOP/s at 2.4 GHz, so the step's own FLOP rate needs at
+    # least value / (2.5e15 / 2.4e9) cycles per second; a lower reading is
+    # flagged.  The profile's SQ busy cycles per microsecond of kernel time
+    # give a second, counter-based figure.
+    if isinstance(clock, dict):
+        floor_mhz = value * 1e12 / (PEAK_BF16_TFLOPS * 1e12 / 2.4e9) / 1e6
+        clock["min_mhz_implied_by_step_rate"] = round(floor_mhz, 1)
+        med = clock.get("gfx_mhz_median")
+        clock["reading_plausible"] = None if med is None else bool(med >= floor_mhz)
+        sq = {k: v.get("sq_busy_ghz") for k, v in prof.items() if v.get("sq_busy_ghz")}
+        if sq:
+            clock["sq_busy_ghz_from_profile"] = sq
 
     kernels = []
     for (n, entry), w, t_all, tw in zip(calls, ws, per_call, warm_ms):
@@ -445,6 +469,7 @@ def main():
     peaks = None
     if not args.no_peaks:
         peaks = attainable_peaks(torch, stream, ws[-1].bytes_alg(2))
+        peaks.pop("_sequence", None)
 
     # dominant kernel = the call with the largest share of step time
     jd = int(np.argmax(per_call_ms))

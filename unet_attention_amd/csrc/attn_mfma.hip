@@ -1017,10 +1017,15 @@ void attn_stream_fix(Args16 a) {
     }
     // fp16 weights must stay below fp16's largest value: when a row's tile
     // maximum rises more than kRescaleSlack above the reference, the
-    // reference moves up.  O still receives tile t-1's weights (taken against
-    // the old reference) in this block, so it is scaled after that P.V.
-    float alpha = 1.f;
-    bool resc = false;
+    // reference moves up.  The tile maximum is computed beside the weights
+    // (nothing waits for it) and checked after the block: in the rare case
+    // the check fires, O -- which now holds tiles up to t-1 against the old
+    // reference -- is scaled and tile t's weights are taken again against
+    // the new one.  (Checking before the weights put the maximum, a
+    // wave-wide vote and a branch ahead of the exponentials, and the
+    // scheduler then ran all vector work of the block before all of its
+    // matrix-core work.)
+    float tmax = 0.f;
     if constexpr (H) {
       f32x16 m0 = cu0, m1 = cu1;
       if constexpr (decltype(mask_c)::value) {
@@ -1030,13 +1035,7 @@ void attn_stream_fix(Args16 a) {
           if (key_tile(t) * BN + 32 + acc_key(i, lane) >= Lk) m1[i] = -__builtin_inff();
         }
       }
-      const float tmax = max_halves(max16(m1, max16(m0, -__builtin_inff()))) * c;
-      if (__any(tmax + nm > kRescaleSlack)) {
-        const float mref = fmaxf(-nm, tmax);
-        alpha = fast_exp2(-nm - mref);
-        nm = -mref;
-        resc = true;
-      }
+      tmax = max_halves(max16(m1, max16(m0, -__builtin_inff()))) * c;
     }
     // The softmax depends on nothing produced in this iteration; an opaque
     // copy of the reference keeps the compiler from hoisting it above the
@@ -1050,11 +1049,19 @@ void attn_stream_fix(Args16 a) {
     weights(mask_c, key_tile(t) * BN, cu0, cu1, nmt, pout);
     if constexpr (HAS_PV) pv(b2, pin);
     if constexpr (H) {
-      if (resc) {
-        asm volatile("");  // a real branch: if-converted, it would scale O every tile
+      if (__any(tmax + nm > kRescaleSlack)) {
+        // A real branch (if-converted it would run every tile); the opaque
+        // use of the first weights keeps the compiler from sinking their
+        // computation out of the block into the path that does not
+        // recompute them.
+        asm volatile("" ::"v"(pout[0]), "v"(pout[1]), "v"(pout[2]), "v"(pout[3]));
+        const float mref = fmaxf(-nm, tmax);
+        const float alpha = fast_exp2(-nm - mref);
+        nm = -mref;
 #pragma unroll
         for (int mt = 0; mt < S::MT; ++mt) o[mt] *= alpha;
         if constexpr (!S::kOnes) lacc *= alpha;
+        weights(mask_c, key_tile(t) * BN, cu0, cu1, nm, pout);
       }
     }
     // The weights are consumed only in the next iteration.  This opaque use
