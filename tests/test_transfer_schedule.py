@@ -7,9 +7,12 @@ Schedule (NB LDS buffers per operand): K tile u goes to buffer u % NB and V
 tile u to buffer u % NB.  Iteration j owns the transfers of K tile j+NB-1
 and V tile j+NB-3 (the prologue plays iterations 1-NB .. -1); iteration t
 reads K tile t+1 (scores) and V tile t-1 (P.V) in its block.  A general
-iteration waits at its own barrier, then issues its own transfers.  In the
-steady-state loop a barrier serves a pair of iterations (t, t+1): it waits
-for the tiles both blocks read, then issues the transfers of both.
+iteration waits at its own barrier and issues its own transfers after its
+block.  In the steady-state loop a barrier serves a pair of iterations
+(t, t+1): it waits for the tiles both blocks read, and each iteration of the
+pair issues its transfers after its block.  Either way a transfer is issued
+after the last barrier before it and before the next one, which is all the
+model below depends on.
 Transfers of one wave complete in issue order, so "vmcnt(c)" at a barrier
 means: everything this wave issued except its last c transfers has landed.
 

@@ -971,23 +971,24 @@ void attn_stream_fix(Args16 a) {
   };
 
   // Iteration t: wait for K tile t+1 and V tile t-1 (owned by iteration
-  // t+2-NB; later ones may stay in flight), issue iteration t's transfers,
-  // then -- one block of independent work -- scores of tile t+1 (into nx),
-  // weights of tile t (from cu, into pout) and P.V of tile t-1 (weights
-  // pin).  Alternate register roles between consecutive iterations avoid
-  // copies.
+  // t+2-NB; later ones may stay in flight), then -- one block of
+  // independent work -- scores of tile t+1 (into nx), weights of tile t
+  // (from cu, into pout) and P.V of tile t-1 (weights pin), then issue
+  // iteration t's transfers (into buffers every wave finished reading before
+  // the last barrier).  Alternate register roles between consecutive
+  // iterations avoid copies.
   // Steady state: one barrier per pair (t, t+1), t odd.  It waits for the
   // tiles of both blocks (owned by iterations up to t+3-NB; the transfers of
-  // the previous pair may stay in flight: later_ss) and issues the transfers
-  // of both iterations (their buffers are read by neither block, NB >= 4);
-  // the pair's second block runs straight on.  Half the barriers and
-  // transfer-issue points of one per iteration (measured: those took ~28 %
-  // of an iteration's cycles on the 64x64-latent workload).
+  // the previous pair may stay in flight: later_ss); the pair's second block
+  // runs straight on, and both iterations issue their transfers after their
+  // blocks (their buffers are read by neither block, NB >= 4).  Half the
+  // barriers of one per iteration (measured: waits and transfer issue took
+  // ~28 % of an iteration's cycles on the 64x64-latent workload).
   const int later_ss = __builtin_amdgcn_readfirstlane((NB - 4) * (kc + vc));
   // PH_c: -1 for the general iteration; else the steady-state form with
   // t % NB == PH (buffer numbers fold to constants; odd PH: first of a
-  // pair, even PH: second) and every transfer of the pair issued (the wait
-  // count is later_ss): far fewer scalar instructions per iteration.
+  // pair, even PH: second) and every transfer issued (the wait count is
+  // later_ss): far fewer scalar instructions per iteration.
   auto body = [&](auto pv_c, auto next_c, auto mask_c, auto ph_c, int t, const f32x16 &cu0,
                   const f32x16 &cu1, f32x16 &nx0, f32x16 &nx1, const u32x4 (&pin)[4],
                   u32x4 (&pout)[4]) {
@@ -996,13 +997,7 @@ void attn_stream_fix(Args16 a) {
     constexpr int PH = decltype(ph_c)::value;
     int b1, b2;  // K buffer read by the scores, V buffer read by P.V
     if constexpr (PH >= 0) {
-      if constexpr (PH % 2 == 1) {
-        vmcnt_barrier_rt<(NB - 4) * P::NIW>(later_ss);
-        issue_k(t + NB - 1, (PH + NB - 1) % NB);
-        issue_v(t + NB - 3, (PH + NB - 3) % NB);
-        issue_k(t + NB, PH);
-        issue_v(t + NB - 2, (PH + NB - 2) % NB);
-      }
+      if constexpr (PH % 2 == 1) vmcnt_barrier_rt<(NB - 4) * P::NIW>(later_ss);
       b1 = (PH + 1) % NB;
       b2 = (PH + NB - 1) % NB;
     } else {
@@ -1013,7 +1008,6 @@ void attn_stream_fix(Args16 a) {
       const int b = t % NB;
       b1 = b == NB - 1 ? 0 : b + 1;
       b2 = b == 0 ? NB - 1 : b - 1;
-      issue_iter(t);
     }
     // fp16 weights must stay below fp16's largest value: when a row's tile
     // maximum rises more than kRescaleSlack above the reference, the
@@ -1069,6 +1063,14 @@ void attn_stream_fix(Args16 a) {
     // barrier: it did so in every other iteration, leaving one block with
     // matrix-core work only and the next with two tiles' vector work.
     asm volatile("" : "+v"(pout[0]), "+v"(pout[1]), "+v"(pout[2]), "+v"(pout[3]));
+    // Iteration t's transfers go out after its block: right after a barrier
+    // every wave would issue at the same moment, with the matrix cores idle.
+    if constexpr (PH >= 0) {
+      issue_k(t + NB - 1, (PH + NB - 1) % NB);
+      issue_v(t + NB - 3, (PH + NB - 3) % NB);
+    } else {
+      issue_iter(t);
+    }
   };
   using F = std::integral_constant<bool, false>;
   using T = std::integral_constant<bool, true>;
@@ -1210,10 +1212,12 @@ void attn_short(Args16 a) {
   constexpr int KCH = (KMAX * S::DK8 + NT - 1) / NT;        // K chunks / thread
   constexpr int VCH = ((KMAX / 4) * S::DK8 + NT - 1) / NT;  // V units / thread
   constexpr int STAGE = kQW * DK * (OUT_F32 ? 4 : 2);            // bytes per wave
-  // Output staging only where K, V^T and the staging area fit in half of the
-  // CU's LDS (two workgroups per CU); otherwise rows are stored directly.
+  // Output staging only where K, V^T and the staging area fit in the LDS
+  // share of one workgroup (half of the CU's for up to four waves: two
+  // workgroups per CU; all of it for eight); otherwise rows are stored
+  // directly.
   constexpr int KV_BYTES = (KMAX * S::KST + S::DV * VST) * 2;
-  constexpr bool kStaged = KV_BYTES + NW * STAGE <= 80 * 1024;
+  constexpr bool kStaged = KV_BYTES + NW * STAGE <= (NW >= 8 ? 160 : 80) * 1024;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KMAX * S::KST];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[S::DV * VST];
   __shared__ __attribute__((aligned(16))) uint8_t Ost[kStaged ? NW * STAGE : 16];
@@ -1383,6 +1387,14 @@ constexpr int kShortTiles = SDATTN_SHORT_TILES;   // query tiles per wave (short
 #define SDATTN_SHORT_NARROW_BELOW 64
 #endif
 constexpr int kShortNarrowBelow = SDATTN_SHORT_NARROW_BELOW;
+// From this many four-wave workgroups on (two waves per SIMD on every CU and
+// more), the short kernel runs eight-wave ones: each workgroup stages the
+// head's keys and values once for twice the query rows, halving the
+// redundant K/V reads from L2.
+#ifndef SDATTN_SHORT_WIDE_FROM
+#define SDATTN_SHORT_WIDE_FROM 512
+#endif
+constexpr int kShortWideFrom = SDATTN_SHORT_WIDE_FROM;
 
 template <int DK, bool H>
 hipError_t launch_short(Args16 a, int BH, bool out_f32, hipStream_t stream) {
@@ -1390,6 +1402,17 @@ hipError_t launch_short(Args16 a, int BH, bool out_f32, hipStream_t stream) {
   const int per_wg = NW * kQW * QPW;
   a.qblocks = (a.Lq + per_wg - 1) / per_wg;
   a.nwg = BH * a.qblocks;
+  if constexpr (NW == 4 && QPW == 1 && waves_per_simd<DK>() == 2) {
+    if (a.nwg >= kShortWideFrom) {
+      constexpr int NW8 = 8;
+      a.qblocks = (a.Lq + NW8 * kQW - 1) / (NW8 * kQW);
+      a.nwg = BH * a.qblocks;
+      const dim3 grid(a.nwg), block(NW8 * kWave);
+      return out_f32
+                 ? launch_kernel(&attn_short<DK, NW8, 1, KMAX, true, H>, grid, block, 0, stream, a)
+                 : launch_kernel(&attn_short<DK, NW8, 1, KMAX, false, H>, grid, block, 0, stream, a);
+    }
+  }
   if constexpr (NW == 4 && QPW == 1) {
     if (a.nwg < kShortNarrowBelow) {
       // few workgroups (the 16x16 level): two-wave workgroups spread the
