@@ -229,10 +229,11 @@ __device__ __forceinline__ void store_out(const f32x16 (&o)[Shape<DK>::MT],
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel, DMA form (default): K and V tiles go from HBM straight
-// into LDS with buffer->LDS transfers, so no registers, LDS writes or vector
-// instructions are spent on staging, and three LDS buffers let the transfer
-// of tile t+2 overlap the computation of tile t.
+// Streaming kernels: K and V tiles go from HBM straight into LDS with
+// buffer->LDS transfers, so no registers, LDS writes or vector instructions
+// are spent on staging, and several LDS buffers (three in the rescaling
+// kernel, six in the fixed-reference one) let the transfers of later tiles
+// overlap the computation of the current one.
 //
 // K keeps its row-major [key][DK+8] layout (the MFMA A operand of S^T is a
 // plain 16-byte LDS read).  V is also kept row-major, [key][VSTR], and the A
