@@ -10,10 +10,12 @@ inputs are seeded N(0,1) synthetic tensors resident in HBM before timing
 starts.
 
 Metric: attention TFLOP/s = 4*B*H*Lq*Lk*d summed over the step's calls,
-divided by the step time.  The JSON line also carries the roofline fraction
-of the dominant kernel (self-attention vs the 16-bit dense MFMA peak, per-launch
-duration from HIP events recorded around each launch on its stream), the
-cross-attention kernel's HBM fraction, and the CPU oracle timed on the host.
+divided by the step time (K steps back to back between two HIP events on
+the launch stream).  The JSON line also carries the roofline fraction of the
+dominant kernel (self-attention vs the 16-bit dense MFMA peak; its per-launch
+duration from HIP events around chunks of that call's launches alone, same
+buffer rotation, on the same stream), the cross-attention kernel's HBM
+fraction, and the CPU oracle timed on the host.
 
 Input sets are rotated across more than 512 MB of buffers so that the
 HBM-bound cross-attention kernel is not served from the 256 MB Infinity
@@ -376,7 +378,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    stream = torch.cuda.current_stream(torch.device("cuda:0"))
+    # a stream of its own (default priority): launches on the legacy null
+    # stream carry its implicit synchronisation
+    stream = torch.cuda.Stream(device=torch.device("cuda:0"))
     st = Step(torch, sd, args.workload, stream)
     calls, ws, nsets = st.calls, st.ws, st.nsets
 
@@ -384,25 +388,46 @@ def main():
         st.launch_set(i)
     torch.cuda.synchronize()
 
-    # timed region: one event on the launch stream before every call and one
-    # after the last, so each call is timed between consecutive events (an
-    # event pair around every call would add its own GPU time to the step);
-    # a call's interval therefore also holds the gap to the next launch
+    # timed region: K steps back to back between two events on the launch
+    # stream (an event recorded between calls costs the step a few
+    # microseconds of GPU time, so none is)
     K = args.steps
     nc = len(calls)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K * nc + 1)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e_start.record(stream)
     for i in range(K):
-        for j, (fn, a) in enumerate(st.argv[i % nsets]):
-            ev[i * nc + j].record(stream)
-            rc = fn(*a)
-            if rc != sd.SDATTN_OK:
-                raise sd.SdattnError(rc, "bench launch")
-    ev[K * nc].record(stream)
+        st.launch_set(i)
+    e_end.record(stream)
     torch.cuda.synchronize()
-    ms_step = ev[0].elapsed_time(ev[K * nc]) / K
-    per_call = [np.array([ev[i * nc + j].elapsed_time(ev[i * nc + j + 1]) for i in range(K)])
-                for j in range(nc)]
+    ms_step = e_start.elapsed_time(e_end) / K
+
+    # per call: the same launches (same buffer rotation) of that call alone,
+    # in chunks timed between two events each; a launch's time therefore
+    # includes the gap to the next launch.  Mean over all chunks, median
+    # and minimum over the chunk means.
+    chunks = 10
+    per_chunk = max(5, K // chunks)
+    per_call = []
+    for j in range(nc):
+        for i in range(5):
+            fn, a = st.argv[i % nsets][j]
+            fn(*a)
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(chunks + 1)]
+        evs[0].record(stream)
+        i = 0
+        for c in range(chunks):
+            for _ in range(per_chunk):
+                fn, a = st.argv[i % nsets][j]
+                rc = fn(*a)
+                if rc != sd.SDATTN_OK:
+                    raise sd.SdattnError(rc, "bench launch")
+                i += 1
+            evs[c + 1].record(stream)
+        torch.cuda.synchronize()
+        per_call.append(np.array([evs[c].elapsed_time(evs[c + 1]) / per_chunk
+                                  for c in range(chunks)]))
     per_call_ms = [float(x.mean()) for x in per_call]
 
     # warm-cache figure: same kernels, one buffer set
@@ -460,7 +485,9 @@ def main():
             "mfma_frac": round(w.flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
             "hbm_frac": round(w.bytes_alg(2) / t / 1e9 / PEAK_HBM_GBS, 4),
             "warm_cache_us": round(tw * 1e3, 3),
-            "timing_note": "event interval to the next launch (includes the launch gap)",
+            "timing_note": "this call alone, back to back, chunks of launches between two events "
+                           "(a launch's time includes the gap to the next launch); median and "
+                           "min over the chunk means",
             "kernel_only_us_rocprof": None if kp is None else kp["avg_us"],
             "hbm_frac_kernel_only": None if kp is None else
             round(w.bytes_alg(2) / (kp["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
@@ -604,7 +631,7 @@ def bench_group_norm(args, name, quiet=False):
     w = GN_WORKLOADS[name]
     x = make_gn_inputs(w)
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
+    stream = torch.cuda.Stream(device=dev)  # its own stream, default priority
     sh = stream.cuda_stream
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
     code = {"bf16": sd.SDATTN_DTYPE_BF16, "f16": sd.SDATTN_DTYPE_F16,
@@ -635,20 +662,18 @@ def bench_group_norm(args, name, quiet=False):
             launch(*sets[i % nsets])
         torch.cuda.synchronize()
         return
+    # K launches back to back between two events (one launch per step; an
+    # event recorded between launches would add its own GPU time)
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         launch(*sets[i % nsets])
-        ev[i][1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / K
-    per_ms = float(np.mean([a.elapsed_time(c) for a, c in ev]))
+    per_ms = ms_step
     nbytes = w.bytes_alg()
     value = nbytes / (ms_step * 1e-3) / 1e9
     ach = nbytes / (per_ms * 1e-3) / 1e9
